@@ -1,0 +1,34 @@
+"""fp64 CPU oracle for content-adaptive block-sparse video attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, obviously-correct
+NumPy (float64) statement of what the hot path computes.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  It shares no code with the HIP library
+(``sparse_attention_long_head_amd``) and never imports it; the two meet only in
+the seeded input generator (``synth``), which holds none of the method's
+arithmetic.
+
+The method (Sparse VideoGen2 explainer, technical summary section 2,
+"Methodology: SVG2"):
+
+* ``kmeans``      -- section 2.a: Q and K are clustered independently with
+  k-means into C_q and C_k clusters.
+* ``permute``     -- section 2.a: tokens are reordered so each cluster is
+  contiguous; the result is equivalent to dense attention.
+* ``select``      -- section 2.b: centroid-pair scores, then clusters are
+  taken in descending score order until their cumulative sum reaches p.
+* ``attention``   -- section 2.c (custom kernel) and section 1 (full 3-D
+  attention): exact softmax attention restricted to the kept blocks, evaluated
+  in original token coordinates (the oracle never permutes).
+
+Every function states its reading of the pages where they are silent.
+Pins (tests under ``tests/test_oracle_*.py``): brute force on tiny inputs,
+scikit-learn's Lloyd k-means, torch's float64 scaled-dot-product attention,
+closed forms, and invariants.  No function here is "parity unpinned".
+"""
+from .kmeans import assign_step, update_step, kmeans, objective, KMeansResult  # noqa: F401
+from .permute import cluster_permutation, permute_rows, unpermute_rows  # noqa: F401
+from .select import centroid_scores, top_p_select, SelectResult  # noqa: F401
+from .attention import (attend, full_attention, cluster_sparse_attention,  # noqa: F401
+                        block_sparse_attention)
+from .pipeline import svg2_layer  # noqa: F401
