@@ -63,8 +63,8 @@ def top_p_select(scores: np.ndarray, size_q: np.ndarray, size_k: np.ndarray,
         w = np.where(valid, size_k * np.exp(np.where(valid, s - smax, 0.0)), 0.0)
         p_row = w / w.sum()
         weights[i] = p_row
-        order = np.lexsort((np.arange(ck), -p_row))     # -P ascending, then id ascending
-        order = order[:n_valid]                          # empty clusters (P = 0) come last
+        cand = np.flatnonzero(valid)                     # empty K clusters are never candidates
+        order = cand[np.lexsort((cand, -p_row[cand]))]   # P descending, then id ascending
         if top_p >= 1.0:
             m = n_valid
         else:

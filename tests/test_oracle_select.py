@@ -114,3 +114,11 @@ def test_kept_mass_is_minimal():
             mass = r.weights[i, kept].sum()
             assert mass >= p - 1e-12
             assert mass - r.weights[i, kept].min() < p
+
+
+def test_underflowed_weight_still_beats_empty_cluster():
+    # cluster 1 is non-empty but its weight underflows to 0; cluster 0 is empty.
+    # With p = 1 every non-empty cluster is kept and the empty one never is.
+    s = np.array([[0.0, -2000.0, 5.0]])
+    r = oracle.top_p_select(s, np.array([1]), np.array([0, 1, 1]), 1.0)
+    assert np.flatnonzero(r.mask[0]).tolist() == [1, 2]
