@@ -1,0 +1,223 @@
+"""Benchmark of one SVG2-form sparse attention layer on one MI355X.
+
+Workload (default): the 5 s clip layer -- 32,760 latent tokens (21x30x52 grid)
+x 40 heads, d=128, bf16; k-means with C_q=100 / C_k=500 for 10 iterations,
+top-p 0.9; seeded synthetic mixture-of-Gaussians tokens (centre scale 1.75,
+about 85% sparsity).  A step is one pass of the whole hot path: k-means of Q
+and of K, permutation of Q and of K/V, top-p selection, block-sparse
+attention, unpermutation.  Inputs are resident in HBM before timing.
+
+Prints one JSON line: value = effective TFLOP/s of the layer (4 d x kept
+(query, key) pairs per step / step time), ms_per_step = ms per layer, plus the
+per-stage breakdown, dense attention on the same tensors, the attention
+kernel's roofline and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms/layer + effective TFLOP/s (frac of bf16 MFMA peak), 32,760 tok x 40 heads"
+ATTN_SRC = os.path.join(ROOT, "sparse_attention_long_head_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_5s_traffic.txt")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attention_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None if
+    the summary is missing or was taken on a different attention kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line)
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if kv.get("attention_source_sha256", "").strip() != src:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, heads=(0, 1, 2)):
+    """The fp64 oracle's whole layer on a few heads (same tensors, same seeds)."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    x = synth.video_qkv(cfg, heads=heads)
+    iq = synth.kmeans_init_indices(cfg, "q", cfg.cq, heads=heads)
+    ik = synth.kmeans_init_indices(cfg, "k", cfg.ck, heads=heads)
+    scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
+    flops = 0.0
+    t0 = time.perf_counter()
+    for j in range(len(heads)):
+        q, k, v = (x[n][0, j].astype(np.float64) for n in "qkv")
+        r = oracle.svg2_layer(q, k, v, q[iq[0, j]], k[ik[0, j]], cfg.iters, cfg.top_p, scale)
+        flops += 4.0 * cfg.d * r["kept_pairs"]
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(heads)} of {cfg.heads} heads, whole layer (k-means x2, select, "
+                      f"masked attention) in fp64 NumPy; {dt:.1f} s; "
+                      f"{dt / len(heads) * cfg.heads * 1e3:.0f} ms/layer extrapolated"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="5s", choices=["5s", "10s", "30s"])
+    ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every stage is independent per head; see the sharding notes in the design "
+              "document).  Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    from sparse_attention_long_head_amd import SparseVideoAttention, sva_full_attn
+
+    cfg = synth.CONFIGS[args.config]
+    if args.top_p is not None:
+        cfg = cfg.with_(top_p=args.top_p)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name}: {cfg.n} tokens x {cfg.heads} heads, d={cfg.d}")
+    x = synth.video_qkv(cfg)
+    init_q = synth.gather_init(x["q"], synth.kmeans_init_indices(cfg, "q", cfg.cq))
+    init_k = synth.gather_init(x["k"], synth.kmeans_init_indices(cfg, "k", cfg.ck))
+    t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv"}
+    iq = torch.from_numpy(init_q).to(dev)
+    ik = torch.from_numpy(init_k).to(dev)
+    del x
+    layer = SparseVideoAttention(cfg.batch, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
+                                 cfg.top_p, device=dev)
+    stages = ("kmeans", "permute", "select", "attention", "unpermute")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        layer.kmeans(t["q"], t["k"], iq, ik)
+        if ev is not None:
+            ev[1].record()
+        layer.permute(t["q"], t["k"], t["v"])
+        if ev is not None:
+            ev[2].record()
+        layer.select()
+        if ev is not None:
+            ev[3].record()
+        layer.attend()
+        if ev is not None:
+            ev[4].record()
+        layer.unpermute()
+        if ev is not None:
+            ev[5].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kept = layer.kept_pairs()
+    density = kept / float(cfg.batch * cfg.heads * cfg.n * cfg.n)
+    flops = 4.0 * cfg.d * kept
+
+    log(f"[bench] timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per_stage = {name: statistics.median(events[s][i].elapsed_time(events[s][i + 1])
+                                         for s in range(args.steps))
+                 for i, name in enumerate(stages)}
+    attn_ms = statistics.mean(events[s][3].elapsed_time(events[s][4]) for s in range(args.steps))
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+
+    dense = None
+    if not args.no_dense:
+        log("[bench] dense attention on the same tensors")
+        o = torch.empty_like(t["q"])
+        sva_full_attn(t["q"], t["k"], t["v"], layer.scale, o=o)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_reps):
+            sva_full_attn(t["q"], t["k"], t["v"], layer.scale, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_reps
+        dense_flops = 4.0 * cfg.d * cfg.batch * cfg.heads * cfg.n * cfg.n
+        dense = {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                 "frac_of_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "speedup_attention_only": dense_ms / attn_ms,
+                 "speedup_whole_layer": dense_ms / ms_step}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] fp64 oracle on a bounded sample (host cores)")
+        cpu = cpu_baseline(cfg)
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    traffic = attention_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded mixture-of-Gaussians video tokens (no dataset)",
+        "config": {"workload": f"svg2 sparse attention layer, {cfg.name} clip",
+                   "tokens": cfg.n, "grid_thw": [cfg.T, cfg.H, cfg.W], "heads": cfg.heads,
+                   "head_dim": cfg.d, "batch": cfg.batch, "cq": cfg.cq, "ck": cfg.ck,
+                   "kmeans_iters": cfg.iters, "top_p": cfg.top_p, "centre_scale": cfg.alpha,
+                   "density": round(density, 5), "kept_pairs": kept},
+        "ms_per_layer": round(ms_step, 4),
+        "frac_of_peak_layer": round(value / PEAK_BF16_TFLOPS, 5),
+        "stages_ms_median": {k: round(v, 4) for k, v in per_stage.items()},
+        "attention": {"ms": round(attn_ms, 4), "effective_tflops": round(attn_tflops, 2),
+                      "frac_of_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
+        "dense": None if dense is None else {k: round(v, 4) for k, v in dense.items()},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,192 @@
+/*
+ * sva.h -- C ABI of libsva, content-adaptive block-sparse self-attention over
+ * the frame x height x width latent tokens of a video diffusion transformer,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows Sparse VideoGen2 (gist.science explainer of
+ * arXiv 2505.18875, technical summary section 2, "Methodology"):
+ *   sva_kmeans            k-means of Q and of K per head            (section 2.a)
+ *   sva_permute           make every cluster contiguous             (section 2.a)
+ *   sva_select_blocks     centroid scores + cumulative top-p        (section 2.b)
+ *   sva_block_sparse_attn attention over the kept blocks only       (section 2.c)
+ *   sva_unpermute         inverse permutation of the output         (section 2.a)
+ * plus the dense baseline sva_full_attn (full 3-D attention, the "VRAM wall" of
+ * the long-video blog, atlascloud.ai, "Why long video is hard").  A fixed mask
+ * over uniform token blocks (DynamicRad explainer, arXiv 2604.20470, technical
+ * summary section 2.a, static-ratio mode) runs through sva_block_sparse_attn
+ * with uniform offsets.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are [batch][heads][n][d], row-major, d fastest, contiguous.
+ *   "bh" below is batch*heads; per-(b,h) arrays are laid out [bh][...].
+ * - All tensor / array pointers are DEVICE pointers owned by the caller.  The
+ *   library never allocates, never frees and never synchronises.  Scratch
+ *   memory is the caller's `ws` buffer of `ws_bytes` bytes; its size comes
+ *   from the matching *_workspace_bytes() query (0 means none is needed, and
+ *   then ws may be NULL).  The workspace holds no state between calls.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call only enqueues work on that stream and returns.
+ * - dtype codes: SVA_F32 (IEEE fp32) or SVA_BF16 (bfloat16).  Supported head
+ *   dims are 64 and 128.
+ * - Errors: every argument is validated on the host before anything is
+ *   launched.  A failed check returns SVA_EINVAL / SVA_EUNSUPPORTED /
+ *   SVA_EWORKSPACE and launches nothing; a HIP launch failure returns
+ *   SVA_EHIP.  sva_last_error() then gives a message (thread-local; valid
+ *   until the next call on the same thread).  Device-side preconditions
+ *   (monotone offsets, in-range indices) are documented per call and are not
+ *   checked on the device.
+ * - Results are deterministic: identical inputs give bitwise-identical
+ *   outputs.  Calls on different streams may overlap if their buffers differ.
+ */
+#ifndef SVA_H
+#define SVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SVA_OK = 0,
+  SVA_EINVAL = 1,        /* bad argument (null pointer, size out of range) */
+  SVA_EUNSUPPORTED = 2,  /* valid but not implemented (e.g. d not 64/128)  */
+  SVA_EWORKSPACE = 3,    /* ws_bytes smaller than the workspace query       */
+  SVA_EHIP = 4           /* a HIP runtime call failed                       */
+};
+
+enum { SVA_F32 = 0, SVA_BF16 = 1 };
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *sva_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t sva_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * sva_kmeans -- Lloyd k-means of every (b,h) slice of x, independently.
+ * Sparse VideoGen2, technical summary section 2.a (Q and K are clustered into
+ * C_q and C_k clusters); section 2.c (centroid cache: the previous step's
+ * centroids seed this one, so the initial centroids are an input).
+ *
+ *   x          [bh][n][d], dtype SVA_BF16 or SVA_F32 (read only)
+ *   c          clusters per slice, 1 <= c <= min(n, 16384)
+ *   iters      Lloyd iterations, >= 1 (exactly this many; no early stop)
+ *   centroids  [bh][c][d] fp32.  IN: initial centroids.  OUT: the means of the
+ *              final assignment (an empty cluster keeps its previous value).
+ *   assign     [bh][n] int32 OUT: cluster of every row in the last iteration,
+ *              argmin of squared Euclidean distance, ties to the lowest index.
+ *   sizes      [bh][c] int32 OUT: rows per cluster in the final assignment.
+ *   n_refined  optional [1] int32 device counter (may be NULL): incremented by
+ *              the number of rows whose assignment was re-decided in fp64
+ *              because the fast MFMA distances could not separate the best
+ *              two clusters.  The caller zeroes it.
+ * Decisions are exact: the fast path carries a rigorous error bound and every
+ * row inside it is re-decided with fp64 distances.
+ * ------------------------------------------------------------------------ */
+size_t sva_kmeans_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t d, int32_t c);
+int32_t sva_kmeans(const void *x, int32_t dtype, int32_t batch, int32_t heads, int32_t n,
+                   int32_t d, int32_t c, int32_t iters, float *centroids, int32_t *assign,
+                   int32_t *sizes, int32_t *n_refined, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_permute -- semantic-aware permutation (Sparse VideoGen2, section 2.a).
+ * A stable counting sort of the rows of each slice by cluster id: clusters in
+ * ascending id, rows of a cluster in ascending original index.
+ *
+ *   assign     [bh][n] int32, values in [0, c) (device precondition)
+ *   perm       [bh][n] int32 OUT: perm[i] = original row of permuted row i
+ *   offsets    [bh][c+1] int32 OUT: cluster j is permuted rows
+ *              [offsets[j], offsets[j+1]); offsets[c] = n
+ *   n_tensors  0, 1 or 2 tensors to gather (e.g. Q alone, or K and V)
+ *   src, dst   HOST arrays of n_tensors DEVICE pointers, each [bh][n][d] of
+ *              `dtype`; dst[t][i] = src[t][perm[i]].  src and dst must not
+ *              overlap.
+ * ------------------------------------------------------------------------ */
+size_t sva_permute_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t c);
+int32_t sva_permute(const int32_t *assign, int32_t c, int32_t batch, int32_t heads, int32_t n,
+                    int32_t d, int32_t dtype, int32_t *perm, int32_t *offsets, int32_t n_tensors,
+                    const void *const *src, void *const *dst, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_select_blocks -- centroid-based top-p (Sparse VideoGen2, section 2.b),
+ * with DynamicRad's rule that a block never ends empty (section 2.a).
+ * For each (b,h) and each Q cluster i with size_q[i] > 0, in fp64:
+ *   S_ij = (cent_q_i . cent_k_j) * scale
+ *   P_ij = size_k[j] exp(S_ij - max) / sum over non-empty K clusters
+ *   order non-empty K clusters by descending P (ties: ascending j) and keep
+ *   the shortest prefix whose cumulative sum is >= top_p (top_p >= 1 keeps
+ *   every non-empty K cluster).  Empty Q clusters keep nothing.
+ *
+ *   cent_q [bh][cq][d] fp32, size_q [bh][cq] int32; likewise cent_k, size_k
+ *   cq, ck     1 <= cq, 1 <= ck <= 4096;  0 < top_p <= 1
+ *   scale, top_p are doubles: the cut is decided in fp64
+ *   mask       [bh][cq][ck] uint8 OUT (1 = kept)
+ *   kept_count [bh][cq] int32 OUT
+ *   kept_idx   [bh][cq][ck] int32 OUT: the kept K ids in ascending order,
+ *              then -1 padding (this compact list is what attention walks)
+ * ------------------------------------------------------------------------ */
+size_t sva_select_workspace_bytes(int32_t batch, int32_t heads, int32_t cq, int32_t ck);
+int32_t sva_select_blocks(const float *cent_q, const int32_t *size_q, int32_t cq,
+                          const float *cent_k, const int32_t *size_k, int32_t ck, int32_t batch,
+                          int32_t heads, int32_t d, double scale, double top_p, uint8_t *mask,
+                          int32_t *kept_count, int32_t *kept_idx, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_block_sparse_attn -- attention over the kept blocks only (Sparse
+ * VideoGen2, section 2.c: dynamic block sizes, contiguous Q computed densely,
+ * K/V of the kept blocks gathered).  For every query row r of Q block i:
+ *   O[r]   = sum over keys n' of the kept K blocks of softmax(q_r.k_n' * scale) v_n'
+ *   LSE[r] = log sum exp(q_r.k_n' * scale)
+ * A row whose block keeps no key gets O = 0 and LSE = -inf.
+ *
+ *   q [bh][n_q][d], k and v [bh][n_k][d]: dtype SVA_BF16 (bf16 MFMA, fp32
+ *              accumulation) or SVA_F32 (fp32 throughout)
+ *   q_offsets  [bh][n_qblocks+1] int32, monotone, q_offsets[0] = 0,
+ *              q_offsets[n_qblocks] = n_q (device precondition)
+ *   k_offsets  [bh][n_kblocks+1] int32, likewise over n_k
+ *   kept_count [bh][n_qblocks] int32 in [0, n_kblocks]
+ *   kept_idx   [bh][n_qblocks][kept_stride] int32; the first kept_count
+ *              entries are distinct K block ids in [0, n_kblocks)
+ *   scale      logit scale (1/sqrt(d) for standard attention)
+ *   o          [bh][n_q][d] OUT, o_dtype SVA_BF16 or SVA_F32
+ *   lse        [bh][n_q] fp32 OUT, natural log; may be NULL
+ * ------------------------------------------------------------------------ */
+size_t sva_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q, int32_t n_qblocks);
+int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32_t dtype,
+                              int32_t batch, int32_t heads, int32_t n_q, int32_t n_k, int32_t d,
+                              const int32_t *q_offsets, int32_t n_qblocks,
+                              const int32_t *k_offsets, int32_t n_kblocks,
+                              const int32_t *kept_count, const int32_t *kept_idx,
+                              int32_t kept_stride, float scale, void *o, int32_t o_dtype,
+                              float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_unpermute -- o[perm[i]] = o_perm[i] per slice (Sparse VideoGen2,
+ * section 2.a: the permuted result is mapped back to token order).
+ *   o_perm, o  [bh][n][d] of dtype (must not overlap); perm [bh][n] int32, a
+ *   permutation of [0, n) (device precondition).
+ * ------------------------------------------------------------------------ */
+int32_t sva_unpermute(const void *o_perm, const int32_t *perm, int32_t dtype, int32_t batch,
+                      int32_t heads, int32_t n, int32_t d, void *o, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_full_attn -- dense softmax attention over all keys (density 1.0), the
+ * baseline the sparse layer is measured against.  Same kernels and the same
+ * numerics as sva_block_sparse_attn with a single block holding every key.
+ * Arguments as in sva_block_sparse_attn.
+ * ------------------------------------------------------------------------ */
+size_t sva_full_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q);
+int32_t sva_full_attn(const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
+                      int32_t heads, int32_t n_q, int32_t n_k, int32_t d, float scale, void *o,
+                      int32_t o_dtype, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVA_H */

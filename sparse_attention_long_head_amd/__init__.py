@@ -1,0 +1,13 @@
+"""MI355X-native content-adaptive block-sparse attention for video DiT latents.
+
+The compute lives in ``libsva.so`` (hand-written HIP for gfx950, C ABI in
+``include/sva.h``); this package is its ctypes binding plus a layer object
+that sequences the calls.  Importing it does not load the library; the first
+call does, and raises if it has not been built.
+"""
+from ._lib import (  # noqa: F401
+    SVA_BF16, SVA_F32, LIB_PATH, lib, last_error,
+    sva_kmeans, sva_permute, sva_select_blocks, sva_block_sparse_attn, sva_unpermute,
+    sva_full_attn,
+)
+from .layer import SparseVideoAttention  # noqa: F401

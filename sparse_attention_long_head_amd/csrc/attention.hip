@@ -1,0 +1,523 @@
+// Block-sparse and dense softmax attention for gfx950.
+//
+// Sparse VideoGen2 (explainer of arXiv 2505.18875, technical summary section
+// 2.c, "customized attention kernel"): query blocks are contiguous clusters
+// that are computed densely, the kept key/value clusters are gathered, and
+// block sizes are dynamic, so no tile is padded to a fixed block size.
+//
+// Design (bf16 path):
+// * One workgroup = 4 waves = one tile of up to 128 query rows of one Q block;
+//   each wave owns 32 query rows, held in registers as the B operand of
+//   S^T = K Q^T (32x32x16 bf16 MFMA).  With keys on the accumulator rows and
+//   queries on lanes, every row max / row sum of the online softmax is
+//   in-lane plus one exchange between the two lane halves.
+// * The kept K blocks of the Q block form one virtual key sequence (their
+//   row ranges concatenated); it is walked in chunks of 64 keys, so a chunk
+//   may span several small clusters and only the very last chunk is partial.
+//   A chunk's K rows go to LDS row-major (16-byte chunks XOR-swizzled) and its
+//   V rows go to LDS transposed, in the key order the PV MFMA consumes, so
+//   every MFMA operand is one conflict-free ds_read_b128.
+// * Global loads of chunk c+1 are issued before the MFMAs of chunk c and
+//   stored to the other LDS buffer after them: one barrier per chunk.
+// * P is rounded to bf16 for the PV MFMA; max, sum and O accumulate in fp32.
+// * Work items are laid out so consecutive items of a head run on one XCD
+//   (workgroups are dispatched round-robin over the 8 XCDs), keeping a head's
+//   K/V in that XCD's L2.
+//
+// The fp32 path is a plain one-thread-per-query kernel (exact fp32, used for
+// small correctness workloads).
+#include <math.h>
+
+#include "../../include/sva.h"
+#include "sva_internal.h"
+
+namespace sva {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQTile = 128;       // query rows per workgroup
+constexpr int kKT = 64;           // keys per chunk
+constexpr int kLCap = 1024;       // kept-list entries staged in LDS at a time
+constexpr int kVS = kKT + 8;      // V^T row stride (elements): 144 B, conflict-free
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct WorkItem {
+  int32_t qb, row0;
+};
+
+// Where chunk-local key k sits inside a V^T row: inside each group of 16 keys,
+// lane half 0 of a PV MFMA consumes keys {0-3, 8-11} and half 1 keys
+// {4-7, 12-15}; storing them as [0-3, 8-11, 4-7, 12-15] makes each half's 8
+// keys contiguous.
+__device__ __forceinline__ int vpos(int k) {
+  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
+}
+
+// XOR swizzle of the 16-byte chunks of K row r (rows of 256 B for d=128,
+// 128 B for d=64) so that 16 lanes reading one chunk column hit 16 banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+__device__ __forceinline__ int find_block(const int32_t *cum, int segn, int v) {
+  int lo = 0, hi = segn - 1;          // largest j with cum[j] <= v
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// In-place exclusive scan of a[0..n) (n <= 4*kThreads) held in LDS; writes
+// the total to a[n].  Must be called by all threads of the workgroup.
+__device__ void block_exclusive_scan(int32_t *a, int n, int32_t *wsum) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int v[4];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (4 * t + i < n) ? a[4 * t + i] : 0;
+    s += v[i];
+  }
+  int x = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int pre = 0;
+  for (int w = 0; w < wave; ++w) pre += wsum[w];
+  int run = pre + x - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * t + i < n) a[4 * t + i] = run;
+    run += v[i];
+  }
+  if (t == kThreads - 1) a[n] = run;
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool decode_work(const WorkItem *work, int work_cap, int n_items,
+                                            int dense, int &bh, int &qb, int &row0) {
+  const int nblk = gridDim.x;   // a multiple of 8
+  const int w = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  if (w >= n_items) return false;
+  bh = w / work_cap;
+  const int slot = w - bh * work_cap;
+  if (dense) {
+    qb = 0;
+    row0 = slot * kQTile;
+    return true;
+  }
+  const WorkItem it = work[w];
+  qb = it.qb;
+  row0 = it.row0;
+  return qb >= 0;
+}
+
+// ---------------------------------------------------------------------------
+// schedule: one work item per 128-row tile of every Q block
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void attn_schedule_kernel(const int32_t *__restrict__ q_off,
+                                                                 int nqb, int work_cap,
+                                                                 WorkItem *__restrict__ work) {
+  __shared__ int32_t wsum[4];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int32_t *off = q_off + static_cast<size_t>(bh) * (nqb + 1);
+  WorkItem *out = work + static_cast<size_t>(bh) * work_cap;
+  int base = 0;
+  for (int b0 = 0; b0 < nqb; b0 += kThreads) {
+    const int qb = b0 + t;
+    int tiles = 0;
+    if (qb < nqb) tiles = max(0, (off[qb + 1] - off[qb] + kQTile - 1) / kQTile);
+    int x = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int pre = 0, total = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) pre += wsum[w];
+      total += wsum[w];
+    }
+    const int first = base + pre + x - tiles;
+    for (int i = 0; i < tiles; ++i)
+      if (first + i < work_cap) out[first + i] = WorkItem{qb, i * kQTile};
+    base += total;
+    __syncthreads();
+  }
+  for (int i = base + t; i < work_cap; i += kThreads) out[i] = WorkItem{-1, -1};
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA attention
+// ---------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, void *__restrict__ o, float *__restrict__ lse,
+    const int32_t *__restrict__ q_off, const int32_t *__restrict__ k_off,
+    const int32_t *__restrict__ kept_count, const int32_t *__restrict__ kept_idx,
+    int kept_stride, const WorkItem *__restrict__ work, int work_cap, int n_items, int n_q,
+    int n_k, int nqb, int nkb, int dense, float scale_log2) {
+  constexpr int KCH = D / 8;             // 16-byte chunks per row
+  constexpr int KCPT = KCH / 4;          // K chunks loaded per thread (4 threads per key)
+  constexpr int VKPT = kKT * D / 8 / kThreads;   // V keys per thread (4 or 2)
+  constexpr int VGROUPS = kKT / VKPT;    // key groups per chunk (16 or 32)
+  constexpr int NS = D / 16;             // k-steps of the S MFMA
+  constexpr int ND = D / 32;             // d tiles of the O accumulator
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kVS];
+  __shared__ int32_t sStart[kLCap];
+  __shared__ int32_t sCum[kLCap + 1];
+  __shared__ int32_t sRow[2][kKT];
+  __shared__ int32_t sWsum[4];
+
+  int bh, qb, row0;
+  if (!decode_work(work, work_cap, n_items, dense, bh, qb, row0)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int qs = dense ? 0 : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb];
+  const int qe = dense ? n_q : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb + 1];
+  const int rbase = qs + row0 + wave * 32;
+  const bool wave_active = rbase < qe;
+  const int myq = rbase + col;
+  const bool qvalid = myq < qe;
+
+  // Q fragments: lane holds Q[myq][16 s + 8 h .. +8]
+  bf16x8 qf[NS];
+  {
+    const uint16_t *qrow = q + (static_cast<size_t>(bh) * n_q + (qvalid ? myq : 0)) * D + h * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4 raw = qvalid ? *reinterpret_cast<const u32x4 *>(qrow + s * 16) : u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kc = dense ? 1 : kept_count[static_cast<size_t>(bh) * nqb + qb];
+  const int32_t *kidx = kept_idx + (static_cast<size_t>(bh) * nqb + qb) * kept_stride;
+  const int32_t *koff = k_off + static_cast<size_t>(bh) * (nkb + 1);
+  const uint16_t *kbase = k + static_cast<size_t>(bh) * n_k * D;
+  const uint16_t *vbase = v + static_cast<size_t>(bh) * n_k * D;
+
+  // register staging of one chunk
+  u32x4 kreg[KCPT];
+  u32x4 vreg[VKPT];
+  const int kk = tid >> 2, kpart = tid & 3;           // K: key, quarter of the row
+  const int vg = tid % VGROUPS, vdg = tid / VGROUPS;   // V: key group, 8-wide d group
+
+  for (int seg0 = 0; seg0 < kc; seg0 += kLCap) {
+    const int segn = min(kLCap, kc - seg0);
+    for (int j = tid; j < segn; j += kThreads) {
+      int st, len;
+      if (dense) {
+        st = 0;
+        len = n_k;
+      } else {
+        const int b = kidx[seg0 + j];
+        st = koff[b];
+        len = koff[b + 1] - st;
+      }
+      sStart[j] = st;
+      sCum[j] = len;
+    }
+    __syncthreads();
+    block_exclusive_scan(sCum, segn, sWsum);
+    const int L = sCum[segn];
+    const int nch = (L + kKT - 1) / kKT;
+    if (nch == 0) continue;   // uniform: L is shared
+
+    auto rowmap = [&](int c, int32_t *dst) {
+      if (tid < kKT) {
+        const int vv = c * kKT + tid;
+        int r = -1;
+        if (vv < L) {
+          const int j = find_block(sCum, segn, vv);
+          r = sStart[j] + (vv - sCum[j]);
+        }
+        dst[tid] = r;
+      }
+    };
+    auto issue_loads = [&](const int32_t *rows) {
+      const int r = rows[kk];
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(kbase + static_cast<size_t>(max(r, 0)) * D) +
+                         kpart * KCPT;
+#pragma unroll
+      for (int i = 0; i < KCPT; ++i) kreg[i] = (r >= 0) ? src[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < VKPT; ++j) {
+        const int rv = rows[vg * VKPT + j];
+        vreg[j] = (rv >= 0) ? *reinterpret_cast<const u32x4 *>(vbase + static_cast<size_t>(rv) * D +
+                                                                vdg * 8)
+                            : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto store_lds = [&](int buf) {
+      uint16_t *kd = sK[buf] + kk * D;
+#pragma unroll
+      for (int i = 0; i < KCPT; ++i) {
+        const int ch = kpart * KCPT + i;
+        *reinterpret_cast<u32x4 *>(kd + ((ch ^ kswz<D>(kk)) * 8)) = kreg[i];
+      }
+      uint16_t *vd = sV[buf] + vpos(vg * VKPT);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int sh = 16 * (dd & 1);
+        if constexpr (VKPT == 4) {
+          const uint32_t e0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu;
+          const uint32_t e1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
+          const uint32_t e2 = (vreg[2][dd >> 1] >> sh) & 0xFFFFu;
+          const uint32_t e3 = (vreg[3][dd >> 1] >> sh) & 0xFFFFu;
+          *reinterpret_cast<u32x2 *>(vd + (vdg * 8 + dd) * kVS) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+        } else {
+          const uint32_t e0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu;
+          const uint32_t e1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
+          *reinterpret_cast<uint32_t *>(vd + (vdg * 8 + dd) * kVS) = e0 | (e1 << 16);
+        }
+      }
+    };
+
+    // prologue
+    rowmap(0, sRow[0]);
+    __syncthreads();
+    issue_loads(sRow[0]);
+    if (nch > 1) rowmap(1, sRow[1]);
+    store_lds(0);
+    __syncthreads();
+
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nch) issue_loads(sRow[buf ^ 1]);
+      if (c + 2 < nch) rowmap(c + 2, sRow[buf]);
+
+      if (wave_active) {
+        // S^T = K Q^T for 64 keys (two 32-key m-tiles)
+        f32x16 sacc[2];
+        const uint16_t *Kb = sK[buf];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          f32x16 acc;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+          const int r = mt * 32 + col;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int ch = 2 * s + h;
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8 *>(Kb + r * D + ((ch ^ kswz<D>(r)) * 8));
+            acc = mfma32x32x16(a, qf[s], acc);
+          }
+          sacc[mt] = acc;
+        }
+        if ((c + 1) * kKT > L) {     // partial last chunk: mask keys past the end
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (c * kKT + mt * 32 + acc_row(i, h) >= L) sacc[mt][i] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * scale_log2);   // finite: chunk has a key
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float ps = 0.f;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], scale_log2, -m_new));
+            ps += p;
+            pb[2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+          }
+        l_run = l_run * alpha + ps;
+        if (__any(m_new > m_run)) {
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        }
+        m_run = m_new;
+        // O^T += V^T P^T
+        const uint16_t *Vb = sV[buf];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8 *>(Vb + (dt * 32 + col) * kVS + ks * 16 + h * 8);
+            oacc[dt] = mfma32x32x16(a, pb[ks], oacc[dt]);
+          }
+      }
+      if (c + 1 < nch) store_lds(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qvalid) {
+    const size_t orow = (static_cast<size_t>(bh) * n_q + myq) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int d0 = dt * 32 + 8 * ig + 4 * h;
+        const float o0 = oacc[dt][4 * ig + 0] * inv, o1 = oacc[dt][4 * ig + 1] * inv;
+        const float o2 = oacc[dt][4 * ig + 2] * inv, o3 = oacc[dt][4 * ig + 3] * inv;
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
+        } else {
+          *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o) + orow + d0) =
+              u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+        }
+      }
+    if (h == 0 && lse != nullptr)
+      lse[static_cast<size_t>(bh) * n_q + myq] =
+          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 attention: one thread per query row, exact fp32 online softmax
+// ---------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kQTile) void attn_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    void *__restrict__ o, float *__restrict__ lse, const int32_t *__restrict__ q_off,
+    const int32_t *__restrict__ k_off, const int32_t *__restrict__ kept_count,
+    const int32_t *__restrict__ kept_idx, int kept_stride, const WorkItem *__restrict__ work,
+    int work_cap, int n_items, int n_q, int n_k, int nqb, int nkb, int dense, float scale) {
+  int bh, qb, row0;
+  if (!decode_work(work, work_cap, n_items, dense, bh, qb, row0)) return;
+  const int qs = dense ? 0 : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb];
+  const int qe = dense ? n_q : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb + 1];
+  const int myq = qs + row0 + threadIdx.x;
+  const bool qvalid = myq < qe;
+  float qv[D], acc[D];
+  const float *qrow = q + (static_cast<size_t>(bh) * n_q + (qvalid ? myq : qs)) * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    qv[i] = qvalid ? qrow[i] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kc = dense ? 1 : kept_count[static_cast<size_t>(bh) * nqb + qb];
+  const int32_t *kidx = kept_idx + (static_cast<size_t>(bh) * nqb + qb) * kept_stride;
+  const int32_t *koff = k_off + static_cast<size_t>(bh) * (nkb + 1);
+  for (int j = 0; j < kc; ++j) {
+    int st = 0, en = n_k;
+    if (!dense) {
+      const int b = kidx[j];
+      st = koff[b];
+      en = koff[b + 1];
+    }
+    for (int key = st; key < en; ++key) {
+      const float *kr = k + (static_cast<size_t>(bh) * n_k + key) * D;
+      const float *vr = v + (static_cast<size_t>(bh) * n_k + key) * D;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) s = fmaf(qv[i], kr[i], s);
+      s *= scale;
+      const float mn = fmaxf(m, s);
+      const float a = expf(m - mn);
+      const float p = expf(s - mn);
+      l = l * a + p;
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc[i] = fmaf(p, vr[i], acc[i] * a);
+      m = mn;
+    }
+  }
+  if (!qvalid) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const size_t orow = (static_cast<size_t>(bh) * n_q + myq) * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    if constexpr (OUT_F32) static_cast<float *>(o)[orow + i] = acc[i] * inv;
+    else static_cast<uint16_t *>(o)[orow + i] = f32_to_bf16_bits(acc[i] * inv);
+  }
+  if (lse != nullptr) lse[static_cast<size_t>(bh) * n_q + myq] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+template <int D, bool OF>
+hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items, int grid,
+                    hipStream_t s) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, OF>), dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+                     static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_off, a.k_off,
+                     a.kept_count, a.kept_idx, a.kept_stride, work, cap, n_items, a.n_q, a.n_k,
+                     a.nqb, a.nkb, a.dense, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool OF>
+hipError_t run_f32(const AttnArgs &a, const WorkItem *work, int cap, int n_items, int grid,
+                   hipStream_t s) {
+  hipLaunchKernelGGL((attn_f32_kernel<D, OF>), dim3(grid), dim3(kQTile), 0, s,
+                     static_cast<const float *>(a.q), static_cast<const float *>(a.k),
+                     static_cast<const float *>(a.v), a.o, a.lse, a.q_off, a.k_off, a.kept_count,
+                     a.kept_idx, a.kept_stride, work, cap, n_items, a.n_q, a.n_k, a.nqb, a.nkb,
+                     a.dense, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_ws_bytes(int32_t bh, int32_t n_q, int32_t nqb) {
+  const size_t cap = static_cast<size_t>((n_q + kQTile - 1) / kQTile) + nqb;
+  return align_up(static_cast<size_t>(bh) * cap * sizeof(WorkItem), 256);
+}
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
+  int cap;
+  const WorkItem *work = nullptr;
+  if (a.dense) {
+    cap = (a.n_q + kQTile - 1) / kQTile;
+  } else {
+    cap = (a.n_q + kQTile - 1) / kQTile + a.nqb;
+    WorkItem *w = static_cast<WorkItem *>(a.ws);
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(a.bh), dim3(kThreads), 0, s, a.q_off, a.nqb,
+                       cap, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    work = w;
+  }
+  const long long n_items = static_cast<long long>(a.bh) * cap;
+  const long long grid = (n_items + 7) / 8 * 8;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const bool of = a.o_dtype == SVA_F32;
+  if (a.dtype == SVA_BF16) {
+    if (a.d == 128) return of ? run_bf16<128, true>(a, work, cap, (int)n_items, (int)grid, s)
+                              : run_bf16<128, false>(a, work, cap, (int)n_items, (int)grid, s);
+    return of ? run_bf16<64, true>(a, work, cap, (int)n_items, (int)grid, s)
+              : run_bf16<64, false>(a, work, cap, (int)n_items, (int)grid, s);
+  }
+  if (a.d == 128) return of ? run_f32<128, true>(a, work, cap, (int)n_items, (int)grid, s)
+                            : run_f32<128, false>(a, work, cap, (int)n_items, (int)grid, s);
+  return of ? run_f32<64, true>(a, work, cap, (int)n_items, (int)grid, s)
+            : run_f32<64, false>(a, work, cap, (int)n_items, (int)grid, s);
+}
+
+}  // namespace sva

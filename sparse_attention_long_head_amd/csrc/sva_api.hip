@@ -1,0 +1,231 @@
+// extern "C" entry points of libsva: host-side validation, workspace carving
+// and kernel dispatch.  Nothing here allocates, frees or synchronises; every
+// check runs before the first launch, so a rejected call launches nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/sva.h"
+#include "sva_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_err.clear();
+  return SVA_OK;
+}
+
+int32_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(SVA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t t) { return t == SVA_F32 || t == SVA_BF16; }
+int32_t elem_bytes(int32_t t) { return t == SVA_F32 ? 4 : 2; }
+
+// shared shape checks; returns SVA_OK or an error status (message set)
+int32_t check_slices(const char *fn, int32_t batch, int32_t heads, int32_t n) {
+  if (batch < 1 || heads < 1) return fail(SVA_EINVAL, "%s: batch and heads must be >= 1", fn);
+  if (static_cast<long long>(batch) * heads > 65535)
+    return fail(SVA_EUNSUPPORTED, "%s: batch*heads must be <= 65535", fn);
+  if (n < 1) return fail(SVA_EINVAL, "%s: n must be >= 1 (got %d)", fn, n);
+  return SVA_OK;
+}
+
+int32_t check_d(const char *fn, int32_t d) {
+  if (d != 64 && d != 128)
+    return fail(SVA_EUNSUPPORTED, "%s: head dim %d not supported (64 or 128)", fn, d);
+  return SVA_OK;
+}
+
+int32_t check_ws(const char *fn, size_t need, const void *ws, size_t ws_bytes) {
+  if (ws_bytes < need)
+    return fail(SVA_EWORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  if (need > 0 && ws == nullptr) return fail(SVA_EINVAL, "%s: ws is NULL", fn);
+  return SVA_OK;
+}
+
+#define SVA_TRY(expr)                    \
+  do {                                   \
+    const int32_t st_ = (expr);          \
+    if (st_ != SVA_OK) return st_;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *sva_last_error(void) { return g_err.c_str(); }
+
+int32_t sva_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------------------
+size_t sva_kmeans_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t d, int32_t c) {
+  if (batch < 1 || heads < 1 || n < 1 || c < 1 || (d != 64 && d != 128)) return 0;
+  return sva::kmeans_ws_bytes(batch * heads, n, d, c);
+}
+
+int32_t sva_kmeans(const void *x, int32_t dtype, int32_t batch, int32_t heads, int32_t n,
+                   int32_t d, int32_t c, int32_t iters, float *centroids, int32_t *assign,
+                   int32_t *sizes, int32_t *n_refined, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "sva_kmeans";
+  if (!x || !centroids || !assign || !sizes)
+    return fail(SVA_EINVAL, "%s: x, centroids, assign and sizes must be non-NULL", fn);
+  if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
+  SVA_TRY(check_slices(fn, batch, heads, n));
+  SVA_TRY(check_d(fn, d));
+  if (c < 1 || c > n) return fail(SVA_EINVAL, "%s: need 1 <= c <= n (c=%d, n=%d)", fn, c, n);
+  if (c > sva::kMaxClustersSort)
+    return fail(SVA_EUNSUPPORTED, "%s: c=%d exceeds %d", fn, c, sva::kMaxClustersSort);
+  if (iters < 1) return fail(SVA_EINVAL, "%s: iters must be >= 1", fn);
+  SVA_TRY(check_ws(fn, sva::kmeans_ws_bytes(batch * heads, n, d, c), ws, ws_bytes));
+  sva::KmeansArgs a{x, dtype, batch * heads, n, d, c, iters, centroids, assign, sizes, n_refined, ws};
+  return hip_status(sva::launch_kmeans(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+size_t sva_permute_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t c) {
+  if (batch < 1 || heads < 1 || n < 1 || c < 1) return 0;
+  return sva::sort_ws_bytes(batch * heads, n, c);
+}
+
+int32_t sva_permute(const int32_t *assign, int32_t c, int32_t batch, int32_t heads, int32_t n,
+                    int32_t d, int32_t dtype, int32_t *perm, int32_t *offsets, int32_t n_tensors,
+                    const void *const *src, void *const *dst, void *ws, size_t ws_bytes,
+                    void *stream) {
+  const char *fn = "sva_permute";
+  if (!assign || !perm || !offsets)
+    return fail(SVA_EINVAL, "%s: assign, perm and offsets must be non-NULL", fn);
+  SVA_TRY(check_slices(fn, batch, heads, n));
+  if (c < 1 || c > n) return fail(SVA_EINVAL, "%s: need 1 <= c <= n (c=%d, n=%d)", fn, c, n);
+  if (c > sva::kMaxClustersSort)
+    return fail(SVA_EUNSUPPORTED, "%s: c=%d exceeds %d", fn, c, sva::kMaxClustersSort);
+  if (n_tensors < 0 || n_tensors > 2) return fail(SVA_EINVAL, "%s: n_tensors must be 0, 1 or 2", fn);
+  if (n_tensors > 0) {
+    if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
+    SVA_TRY(check_d(fn, d));
+    if (!src || !dst) return fail(SVA_EINVAL, "%s: src and dst arrays must be non-NULL", fn);
+    for (int t = 0; t < n_tensors; ++t)
+      if (!src[t] || !dst[t]) return fail(SVA_EINVAL, "%s: tensor pointer %d is NULL", fn, t);
+  }
+  SVA_TRY(check_ws(fn, sva::sort_ws_bytes(batch * heads, n, c), ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bh = batch * heads;
+  hipError_t e = sva::launch_cluster_sort(assign, bh, n, c, perm, offsets, nullptr, ws, s);
+  for (int t = 0; t < n_tensors && e == hipSuccess; ++t)
+    e = sva::launch_gather_rows(src[t], dst[t], perm, bh, n, d * elem_bytes(dtype), 0, s);
+  return hip_status(e, fn);
+}
+
+// ---------------------------------------------------------------------------
+size_t sva_select_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+int32_t sva_select_blocks(const float *cent_q, const int32_t *size_q, int32_t cq,
+                          const float *cent_k, const int32_t *size_k, int32_t ck, int32_t batch,
+                          int32_t heads, int32_t d, double scale, double top_p, uint8_t *mask,
+                          int32_t *kept_count, int32_t *kept_idx, void *ws, size_t ws_bytes,
+                          void *stream) {
+  const char *fn = "sva_select_blocks";
+  (void)ws;
+  (void)ws_bytes;
+  if (!cent_q || !size_q || !cent_k || !size_k || !mask || !kept_count || !kept_idx)
+    return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_slices(fn, batch, heads, 1));
+  SVA_TRY(check_d(fn, d));
+  if (cq < 1 || ck < 1) return fail(SVA_EINVAL, "%s: cq and ck must be >= 1", fn);
+  if (ck > sva::kMaxSelectK)
+    return fail(SVA_EUNSUPPORTED, "%s: ck=%d exceeds %d", fn, ck, sva::kMaxSelectK);
+  if (!(top_p > 0.0 && top_p <= 1.0))
+    return fail(SVA_EINVAL, "%s: top_p must be in (0, 1] (got %g)", fn, top_p);
+  if (!isfinite(scale)) return fail(SVA_EINVAL, "%s: scale must be finite", fn);
+  sva::SelectArgs a{cent_q, cent_k, size_q, size_k, batch * heads, cq, ck, d, scale, top_p,
+                    mask, kept_count, kept_idx};
+  return hip_status(sva::launch_select(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+static int32_t check_attn(const char *fn, const void *q, const void *k, const void *v,
+                          int32_t dtype, int32_t batch, int32_t heads, int32_t n_q, int32_t n_k,
+                          int32_t d, float scale, const void *o, int32_t o_dtype) {
+  if (!q || !k || !v || !o) return fail(SVA_EINVAL, "%s: q, k, v and o must be non-NULL", fn);
+  if (!dtype_ok(dtype) || !dtype_ok(o_dtype))
+    return fail(SVA_EINVAL, "%s: bad dtype (%d) or o_dtype (%d)", fn, dtype, o_dtype);
+  SVA_TRY(check_slices(fn, batch, heads, n_q));
+  if (n_k < 1) return fail(SVA_EINVAL, "%s: n_k must be >= 1", fn);
+  SVA_TRY(check_d(fn, d));
+  if (!isfinite(scale)) return fail(SVA_EINVAL, "%s: scale must be finite", fn);
+  return SVA_OK;
+}
+
+size_t sva_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q, int32_t n_qblocks) {
+  if (batch < 1 || heads < 1 || n_q < 1 || n_qblocks < 1) return 0;
+  return sva::attn_ws_bytes(batch * heads, n_q, n_qblocks);
+}
+
+int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32_t dtype,
+                              int32_t batch, int32_t heads, int32_t n_q, int32_t n_k, int32_t d,
+                              const int32_t *q_offsets, int32_t n_qblocks,
+                              const int32_t *k_offsets, int32_t n_kblocks,
+                              const int32_t *kept_count, const int32_t *kept_idx,
+                              int32_t kept_stride, float scale, void *o, int32_t o_dtype,
+                              float *lse, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "sva_block_sparse_attn";
+  SVA_TRY(check_attn(fn, q, k, v, dtype, batch, heads, n_q, n_k, d, scale, o, o_dtype));
+  if (!q_offsets || !k_offsets || !kept_count || !kept_idx)
+    return fail(SVA_EINVAL, "%s: offsets and kept lists must be non-NULL", fn);
+  if (n_qblocks < 1 || n_qblocks > n_q)
+    return fail(SVA_EINVAL, "%s: need 1 <= n_qblocks <= n_q", fn);
+  if (n_kblocks < 1 || n_kblocks > n_k)
+    return fail(SVA_EINVAL, "%s: need 1 <= n_kblocks <= n_k", fn);
+  if (kept_stride < 1) return fail(SVA_EINVAL, "%s: kept_stride must be >= 1", fn);
+  const long long items = static_cast<long long>(batch) * heads * ((n_q + 127) / 128 + n_qblocks);
+  if (items > 0x7ffffff0LL) return fail(SVA_EUNSUPPORTED, "%s: problem too large for one launch", fn);
+  SVA_TRY(check_ws(fn, sva::attn_ws_bytes(batch * heads, n_q, n_qblocks), ws, ws_bytes));
+  sva::AttnArgs a{q, k, v, o, lse, q_offsets, k_offsets, kept_count, kept_idx, kept_stride,
+                  batch * heads, n_q, n_k, d, n_qblocks, n_kblocks, dtype, o_dtype, 0, scale, ws};
+  return hip_status(sva::launch_attention(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t sva_full_attn_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+
+int32_t sva_full_attn(const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
+                      int32_t heads, int32_t n_q, int32_t n_k, int32_t d, float scale, void *o,
+                      int32_t o_dtype, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "sva_full_attn";
+  (void)ws;
+  (void)ws_bytes;
+  SVA_TRY(check_attn(fn, q, k, v, dtype, batch, heads, n_q, n_k, d, scale, o, o_dtype));
+  sva::AttnArgs a{q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, 0,
+                  batch * heads, n_q, n_k, d, 1, 1, dtype, o_dtype, 1, scale, nullptr};
+  return hip_status(sva::launch_attention(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+int32_t sva_unpermute(const void *o_perm, const int32_t *perm, int32_t dtype, int32_t batch,
+                      int32_t heads, int32_t n, int32_t d, void *o, void *stream) {
+  const char *fn = "sva_unpermute";
+  if (!o_perm || !perm || !o) return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
+  SVA_TRY(check_slices(fn, batch, heads, n));
+  SVA_TRY(check_d(fn, d));
+  return hip_status(sva::launch_gather_rows(o_perm, o, perm, batch * heads, n,
+                                            d * elem_bytes(dtype), 1,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+"""One SVG2-form sparse attention layer as a sequence of libsva calls.
+
+Sparse VideoGen2 explainer, technical summary section 2: k-means of Q and K
+(2.a), permutation so that clusters are contiguous (2.a), centroid top-p
+(2.b), attention over the kept blocks (2.c), inverse permutation (2.a).
+
+``SparseVideoAttention`` owns every buffer the layer needs (allocated once,
+through torch), so ``forward`` only enqueues the seven library calls on the
+current stream: it allocates nothing and never synchronises.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+class SparseVideoAttention:
+    def __init__(self, batch: int, heads: int, n: int, d: int, cq: int, ck: int, iters: int,
+                 top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda",
+                 scale: Optional[float] = None, want_lse: bool = False):
+        self.shape = (batch, heads, n, d)
+        self.cq, self.ck, self.iters, self.top_p = cq, ck, iters, top_p
+        # a float32-representable scale, so the fp64 selection and the fp32
+        # attention kernels use the identical value
+        self.scale = float(np.float32(1.0 / math.sqrt(d) if scale is None else scale))
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.cent_q = torch.empty((batch, heads, cq, d), **f32)
+        self.cent_k = torch.empty((batch, heads, ck, d), **f32)
+        self.assign_q = torch.empty((batch, heads, n), **i32)
+        self.assign_k = torch.empty((batch, heads, n), **i32)
+        self.sizes_q = torch.empty((batch, heads, cq), **i32)
+        self.sizes_k = torch.empty((batch, heads, ck), **i32)
+        self.perm_q = torch.empty((batch, heads, n), **i32)
+        self.perm_k = torch.empty((batch, heads, n), **i32)
+        self.off_q = torch.empty((batch, heads, cq + 1), **i32)
+        self.off_k = torch.empty((batch, heads, ck + 1), **i32)
+        self.q_p = torch.empty(self.shape, dtype=dtype, device=dev)
+        self.k_p = torch.empty(self.shape, dtype=dtype, device=dev)
+        self.v_p = torch.empty(self.shape, dtype=dtype, device=dev)
+        self.mask = torch.empty((batch, heads, cq, ck), dtype=torch.uint8, device=dev)
+        self.kept_count = torch.empty((batch, heads, cq), **i32)
+        self.kept_idx = torch.empty((batch, heads, cq, ck), **i32)
+        self.o_p = torch.empty(self.shape, dtype=dtype, device=dev)
+        self.o = torch.empty(self.shape, dtype=dtype, device=dev)
+        # LSE of the permuted query rows (row i belongs to token perm_q[i])
+        self.lse_p = torch.empty((batch, heads, n), **f32) if want_lse else None
+        lib = L.lib()
+        km = max(lib.sva_kmeans_workspace_bytes(batch, heads, n, d, cq),
+                 lib.sva_kmeans_workspace_bytes(batch, heads, n, d, ck))
+        pm = max(lib.sva_permute_workspace_bytes(batch, heads, n, cq),
+                 lib.sva_permute_workspace_bytes(batch, heads, n, ck))
+        at = lib.sva_attn_workspace_bytes(batch, heads, n, cq)
+        self.ws = torch.empty(max(km, pm, at, 1), dtype=torch.uint8, device=dev)
+
+    # the individual stages, so callers (and the benchmark) can time them
+    def kmeans(self, q, k, init_q, init_k):
+        self.cent_q.copy_(init_q)
+        self.cent_k.copy_(init_k)
+        L.sva_kmeans(q, self.cq, self.iters, self.cent_q, self.assign_q, self.sizes_q, ws=self.ws)
+        L.sva_kmeans(k, self.ck, self.iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
+
+    def permute(self, q, k, v):
+        L.sva_permute(self.assign_q, self.cq, [q], self.perm_q, self.off_q, [self.q_p], ws=self.ws)
+        L.sva_permute(self.assign_k, self.ck, [k, v], self.perm_k, self.off_k,
+                      [self.k_p, self.v_p], ws=self.ws)
+
+    def select(self):
+        L.sva_select_blocks(self.cent_q, self.sizes_q, self.cent_k, self.sizes_k, self.scale,
+                            self.top_p, self.mask, self.kept_count, self.kept_idx)
+
+    def attend(self):
+        L.sva_block_sparse_attn(self.q_p, self.k_p, self.v_p, self.off_q, self.off_k,
+                                self.kept_count, self.kept_idx, self.scale, o=self.o_p,
+                                lse=self.lse_p, ws=self.ws)
+
+    def unpermute(self):
+        L.sva_unpermute(self.o_p, self.perm_q, self.o)
+
+    def forward(self, q, k, v, init_q, init_k) -> torch.Tensor:
+        self.kmeans(q, k, init_q, init_k)
+        self.permute(q, k, v)
+        self.select()
+        self.attend()
+        self.unpermute()
+        return self.o
+
+    __call__ = forward
+
+    def kept_pairs(self) -> int:
+        """(query, key) pairs the mask allows; synchronises (host read-back)."""
+        sq = self.sizes_q.cpu().numpy().astype(np.int64)
+        sk = self.sizes_k.cpu().numpy().astype(np.int64)
+        m = self.mask.cpu().numpy().astype(np.int64)
+        return int(np.einsum("bhi,bhij,bhj->", sq, m, sk))

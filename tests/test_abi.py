@@ -1,0 +1,117 @@
+"""The C ABI on the host (no GPU needed): the library builds and loads, exports
+every entry point include/sva.h declares, and rejects bad arguments with the
+documented status before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_attention_long_head_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_long_head_amd import build
+        build.build()
+    _lib.lib()
+    return _lib
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "sva.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(sva_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sva_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert n in L.SIGNATURES, f"binding lacks {n}"
+    assert L.lib().sva_abi_version() == 1
+
+
+P = ctypes.c_void_p(256)   # a non-NULL dummy: nothing may be dereferenced before validation
+
+
+def test_kmeans_validation(L):
+    lib = L.lib()
+    ws = lib.sva_kmeans_workspace_bytes(1, 2, 1000, 128, 10)
+    assert ws > 0
+    cases = [
+        ((None, 1, 1, 2, 1000, 128, 10, 3, P, P, P, None, P, ws, None), L.SVA_EINVAL),
+        ((P, 7, 1, 2, 1000, 128, 10, 3, P, P, P, None, P, ws, None), L.SVA_EINVAL),
+        ((P, 1, 1, 2, 1000, 96, 10, 3, P, P, P, None, P, ws, None), L.SVA_EUNSUPPORTED),
+        ((P, 1, 1, 2, 1000, 128, 0, 3, P, P, P, None, P, ws, None), L.SVA_EINVAL),
+        ((P, 1, 1, 2, 1000, 128, 1001, 3, P, P, P, None, P, ws, None), L.SVA_EINVAL),
+        ((P, 1, 1, 2, 1000, 128, 10, 0, P, P, P, None, P, ws, None), L.SVA_EINVAL),
+        ((P, 1, 1, 2, 1000, 128, 10, 3, P, P, P, None, P, ws - 1, None), L.SVA_EWORKSPACE),
+        ((P, 1, 1, 2, 1000, 128, 10, 3, P, P, P, None, None, ws, None), L.SVA_EINVAL),
+        ((P, 1, 0, 2, 1000, 128, 10, 3, P, P, P, None, P, ws, None), L.SVA_EINVAL),
+        ((P, 1, 1, 70000, 1000, 128, 10, 3, P, P, P, None, P, ws, None), L.SVA_EUNSUPPORTED),
+    ]
+    for args, want in cases:
+        assert lib.sva_kmeans(*args) == want, args
+        assert L.last_error().startswith("sva_kmeans")
+
+
+def test_permute_validation(L):
+    lib = L.lib()
+    ws = lib.sva_permute_workspace_bytes(1, 1, 100, 7)
+    src = (ctypes.c_void_p * 2)(256, 512)
+    bad = (ctypes.c_void_p * 2)(256, None)
+    assert lib.sva_permute(P, 7, 1, 1, 100, 128, 1, P, P, 3, src, src, P, ws, None) == L.SVA_EINVAL
+    assert lib.sva_permute(P, 0, 1, 1, 100, 128, 1, P, P, 1, src, src, P, ws, None) == L.SVA_EINVAL
+    assert lib.sva_permute(P, 7, 1, 1, 100, 128, 1, P, P, 2, src, bad, P, ws, None) == L.SVA_EINVAL
+    assert lib.sva_permute(P, 7, 1, 1, 100, 32, 1, P, P, 1, src, src, P, ws, None) \
+        == L.SVA_EUNSUPPORTED
+    assert lib.sva_permute(P, 7, 1, 1, 100, 128, 1, P, P, 1, src, src, P, ws - 4, None) \
+        == L.SVA_EWORKSPACE
+    assert lib.sva_permute(P, 20000, 1, 1, 30000, 128, 1, P, P, 0, None, None, P, 1 << 30,
+                           None) == L.SVA_EUNSUPPORTED
+
+
+def test_select_validation(L):
+    lib = L.lib()
+    ok = (P, P, 10, P, P, 20, 1, 2, 128, 0.1, 0.9, P, P, P, None, 0, None)
+    for i, bad, want in [(10, 0.0, L.SVA_EINVAL), (10, 1.5, L.SVA_EINVAL),
+                         (10, float("nan"), L.SVA_EINVAL), (5, 5000, L.SVA_EUNSUPPORTED),
+                         (8, 64 + 1, L.SVA_EUNSUPPORTED), (0, None, L.SVA_EINVAL),
+                         (9, float("inf"), L.SVA_EINVAL)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.sva_select_blocks(*args) == want, (i, bad)
+
+
+def test_attention_validation(L):
+    lib = L.lib()
+    ws = lib.sva_attn_workspace_bytes(1, 2, 1000, 8)
+    ok = [P, P, P, 1, 1, 2, 1000, 1000, 128, P, 8, P, 8, P, P, 8, 0.1, P, 1, None, P, ws, None]
+    for i, bad, want in [(0, None, L.SVA_EINVAL), (3, 5, L.SVA_EINVAL), (8, 80, L.SVA_EUNSUPPORTED),
+                         (10, 0, L.SVA_EINVAL), (10, 1001, L.SVA_EINVAL), (12, 0, L.SVA_EINVAL),
+                         (15, 0, L.SVA_EINVAL), (16, float("nan"), L.SVA_EINVAL),
+                         (18, 9, L.SVA_EINVAL), (21, ws - 1, L.SVA_EWORKSPACE),
+                         (13, None, L.SVA_EINVAL)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.sva_block_sparse_attn(*args) == want, (i, bad)
+    assert lib.sva_full_attn(P, P, P, 1, 1, 2, 10, 10, 64, float("inf"), P, 1, None, None, 0,
+                             None) == L.SVA_EINVAL
+    assert lib.sva_unpermute(P, None, 1, 1, 1, 10, 64, P, None) == L.SVA_EINVAL
+    assert "sva_unpermute" in L.last_error()
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from sparse_attention_long_head_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,213 @@
+"""GPU parity of sva_full_attn and sva_block_sparse_attn against the fp64 oracle.
+
+Tolerance derivation (bf16 inputs, fp32 accumulation): logits are exact
+products summed in fp32 (relative error ~1e-6); P is rounded to bf16 before the
+PV product (relative 2^-9 per weight, averaging out over the kept keys); the
+output rounds to bf16 (half an ulp: up to 2^-9 relative, i.e. ~1.6e-2 absolute
+for |O| near 2..4 and ~1.1e-3 mean for N(0,1)-sized outputs).  The contract
+bounds are max-abs 2e-2 and mean-abs 2e-3 in bf16 mode and 1e-4 in fp32 mode;
+LSE is checked to 1e-3 (bf16) / 1e-5 (fp32) absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (check_attention, check_lse, device, host, rand_inputs, to_dev)
+from sparse_attention_long_head_amd import sva_block_sparse_attn, sva_full_attn
+
+pytestmark = pytest.mark.gpu
+
+
+def _tdtype(bf16):
+    return torch.bfloat16 if bf16 else torch.float32
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nq,nk", [(256, 256), (300, 333), (1, 1), (129, 5), (1000, 64)])
+def test_full_attention(bf16, d, nq, nk):
+    h = 2
+    dt = "bf16" if bf16 else "f32"
+    q = rand_inputs((1, h, nq, d), 1, dt)
+    k = rand_inputs((1, h, nk, d), 2, dt)
+    v = rand_inputs((1, h, nk, d), 3, dt)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = sva_full_attn(to_dev(q, _tdtype(bf16)), to_dev(k, _tdtype(bf16)),
+                           to_dev(v, _tdtype(bf16)), scale, want_lse=True)
+    o, lse = host(o), host(lse)
+    for hh in range(h):
+        ro, rl = oracle.full_attention(q[0, hh], k[0, hh], v[0, hh], np.float32(scale))
+        check_attention(o[0, hh], ro, bf16, f"head {hh}")
+        check_lse(lse[0, hh], rl, 1e-3 if bf16 else 1e-5)
+
+
+def test_full_attention_fp32_output_of_bf16_inputs():
+    q, k, v = (rand_inputs((1, 1, 700, 128), s) for s in (4, 5, 6))
+    o, _ = sva_full_attn(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
+                         to_dev(v, torch.bfloat16), 1 / math.sqrt(128), o_dtype=torch.float32)
+    ro, _ = oracle.full_attention(q[0, 0], k[0, 0], v[0, 0], np.float32(1 / math.sqrt(128)))
+    err = np.abs(host(o)[0, 0] - ro)
+    # without the final bf16 rounding only the kernel's own error remains
+    assert err.max() < 4e-3 and err.mean() < 3e-4, (err.max(), err.mean())
+
+
+def _uniform_case(n, block, heads, seed, density, bf16, d):
+    rng = np.random.default_rng(seed)
+    nb = -(-n // block)
+    masks = rng.random((heads, nb, nb)) < density
+    masks[:, np.arange(nb), np.arange(nb)] = True
+    masks[0, nb - 1, :] = False          # one query block keeps nothing
+    dt = "bf16" if bf16 else "f32"
+    q, k, v = (rand_inputs((1, heads, n, d), seed + i, dt) for i in range(3))
+    off = np.tile(synth.uniform_offsets(n, block), (1, heads, 1))
+    cnt, idx = synth.mask_to_ell(masks[None])
+    return q, k, v, masks, off, cnt, idx
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_uniform_blocks_ragged(bf16, d):
+    n, block, heads = 1000, 128, 3
+    q, k, v, masks, off, cnt, idx = _uniform_case(n, block, heads, 11, 0.4, bf16, d)
+    T = _tdtype(bf16)
+    scale = 1 / math.sqrt(d)
+    o, lse = sva_block_sparse_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T),
+                                   to_dev(off, torch.int32), to_dev(off, torch.int32),
+                                   to_dev(cnt, torch.int32), to_dev(idx, torch.int32), scale,
+                                   want_lse=True)
+    o, lse = host(o), host(lse)
+    for h in range(heads):
+        ro, rl = oracle.block_sparse_attention(q[0, h], k[0, h], v[0, h], masks[h], block,
+                                               np.float32(scale))
+        check_attention(o[0, h], ro, bf16, f"head {h}")
+        check_lse(lse[0, h], rl, 1e-3 if bf16 else 1e-5)
+    # the query block that keeps nothing: O = 0, LSE = -inf
+    assert (o[0, 0, 896:] == 0).all() and np.isneginf(lse[0, 0, 896:]).all()
+
+
+def _random_partition(n, nb, rng, extreme=True):
+    cuts = np.sort(rng.integers(0, n + 1, nb - 1))
+    if extreme and nb > 4:
+        cuts[0] = cuts[1]            # an empty block
+        cuts[2] = max(cuts[1], cuts[3] - 1)   # often a 1-row block
+    off = np.concatenate([[0], cuts, [n]]).astype(np.int32)
+    return off
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_variable_blocks(bf16, seed):
+    rng = np.random.default_rng(seed)
+    heads, d, nq, nk, nqb, nkb = 2, 128, 777, 901, 9, 23
+    dt = "bf16" if bf16 else "f32"
+    q = rand_inputs((1, heads, nq, d), 20 + seed, dt)
+    k = rand_inputs((1, heads, nk, d), 30 + seed, dt)
+    v = rand_inputs((1, heads, nk, d), 40 + seed, dt)
+    qoff = np.stack([_random_partition(nq, nqb, rng) for _ in range(heads)])[None]
+    koff = np.stack([_random_partition(nk, nkb, rng) for _ in range(heads)])[None]
+    masks = rng.random((1, heads, nqb, nkb)) < 0.35
+    masks[0, 0, 1] = False
+    cnt, idx = synth.mask_to_ell(masks)
+    T = _tdtype(bf16)
+    scale = 1 / math.sqrt(d)
+    o, lse = sva_block_sparse_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T),
+                                   to_dev(qoff, torch.int32), to_dev(koff, torch.int32),
+                                   to_dev(cnt, torch.int32), to_dev(idx, torch.int32), scale,
+                                   want_lse=True)
+    o, lse = host(o), host(lse)
+    for h in range(heads):
+        aq = np.repeat(np.arange(nqb), np.diff(qoff[0, h]))
+        ak = np.repeat(np.arange(nkb), np.diff(koff[0, h]))
+        ro, rl = oracle.cluster_sparse_attention(q[0, h], k[0, h], v[0, h], aq, ak, masks[0, h],
+                                                 np.float32(scale))
+        check_attention(o[0, h], ro, bf16, f"head {h}")
+        check_lse(lse[0, h], rl, 1e-3 if bf16 else 1e-5)
+
+
+def test_kept_list_longer_than_one_lds_segment():
+    # 1300 two-key blocks, all kept: the kept list is walked in several segments
+    rng = np.random.default_rng(5)
+    d, nq, nkb = 128, 200, 1300
+    nk = 2 * nkb
+    q = rand_inputs((1, 1, nq, d), 50)
+    k = rand_inputs((1, 1, nk, d), 51)
+    v = rand_inputs((1, 1, nk, d), 52)
+    qoff = np.array([[[0, 77, nq]]], np.int32)
+    koff = (2 * np.arange(nkb + 1, dtype=np.int32))[None, None]
+    masks = np.ones((1, 1, 2, nkb), bool)
+    masks[0, 0, 1] = rng.random(nkb) < 0.85
+    cnt, idx = synth.mask_to_ell(masks)
+    scale = 1 / math.sqrt(d)
+    o, _ = sva_block_sparse_attn(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
+                                 to_dev(v, torch.bfloat16), to_dev(qoff, torch.int32),
+                                 to_dev(koff, torch.int32), to_dev(cnt, torch.int32),
+                                 to_dev(idx, torch.int32), scale)
+    aq = np.repeat(np.arange(2), np.diff(qoff[0, 0]))
+    ak = np.repeat(np.arange(nkb), 2)
+    ro, _ = oracle.cluster_sparse_attention(q[0, 0], k[0, 0], v[0, 0], aq, ak, masks[0, 0],
+                                            np.float32(scale))
+    check_attention(host(o)[0, 0], ro, True)
+
+
+def test_deterministic():
+    q, k, v, masks, off, cnt, idx = _uniform_case(1500, 128, 2, 3, 0.3, True, 128)
+    args = [to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16),
+            to_dev(off, torch.int32), to_dev(off, torch.int32), to_dev(cnt, torch.int32),
+            to_dev(idx, torch.int32), 0.088]
+    a, _ = sva_block_sparse_attn(*args)
+    b, _ = sva_block_sparse_attn(*args)
+    assert torch.equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def static_full():
+    """The static-mask workload at full size: 32,760 tokens x 40 heads, d=128,
+    i.i.d. N(0,1) bf16, radial + random mask at 80% sparsity (shared by heads)."""
+    cfg = synth.CONFIGS["static"]
+    x = synth.video_qkv(cfg)
+    mask = synth.static_block_mask(cfg)
+    return cfg, x, mask
+
+
+def _sample_rows(n, rng, k=24):
+    fixed = [0, 1, 127, 128, 255, n // 2, n - 121, n - 120, n - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, n, k)]))
+
+
+def test_static_config_full_size_sampled(static_full):
+    cfg, x, mask = static_full
+    dev = device()
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv")
+    off = np.tile(synth.uniform_offsets(cfg.n, cfg.block), (1, cfg.heads, 1))
+    cnt, idx = synth.mask_to_ell(np.broadcast_to(mask, (1, cfg.heads) + mask.shape))
+    scale = 1 / math.sqrt(cfg.d)
+    o, lse = sva_block_sparse_attn(q, k, v, to_dev(off, torch.int32), to_dev(off, torch.int32),
+                                   to_dev(cnt, torch.int32), to_dev(idx, torch.int32), scale,
+                                   want_lse=True)
+    o, lse = host(o), host(lse)
+    rng = np.random.default_rng(0)
+    for h in (0, 17, 39):
+        rows = _sample_rows(cfg.n, rng)
+        ro, rl = oracle.block_sparse_attention(x["q"][0, h], x["k"][0, h], x["v"][0, h], mask,
+                                               cfg.block, np.float32(scale), rows=rows)
+        check_attention(o[0, h, rows], ro, True, f"static head {h}")
+        check_lse(lse[0, h, rows], rl, 1e-3)
+
+
+def test_dense_full_size_sampled(static_full):
+    cfg, x, _ = static_full
+    dev = device()
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv")
+    scale = 1 / math.sqrt(cfg.d)
+    o, _ = sva_full_attn(q, k, v, scale)
+    o = host(o)
+    rng = np.random.default_rng(1)
+    for h in (3, 38):
+        rows = _sample_rows(cfg.n, rng, 8)
+        ro, _ = oracle.full_attention(x["q"][0, h], x["k"][0, h], x["v"][0, h],
+                                      np.float32(scale), rows=rows)
+        check_attention(o[0, h, rows], ro, True, f"dense head {h}")

@@ -1,0 +1,122 @@
+"""GPU parity of sva_kmeans against the fp64 Lloyd oracle.
+
+Lockstep: each GPU iteration (iters=1, centroids in/out) is compared with the
+oracle's assignment step on the GPU's input centroids (exact, except rows whose
+fp64 top-2 margin is below 1e-5, which are counted) and the oracle's update
+step on the GPU's assignment (the GPU sums in fp64 and rounds the mean to
+fp32 once, so centroids agree to an ulp of fp32).  Chained runs (10 iterations
+on each side) report how many assignments a near-tie cascade changed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import TIE, assign_parity, device, host, to_dev
+from sparse_attention_long_head_amd import sva_kmeans
+
+pytestmark = pytest.mark.gpu
+
+
+def _lockstep(x, init, c, iters, dtype, heads=None):
+    """x float32 [1, H, n, d] (exact values); returns tie-mismatch count."""
+    dev = device()
+    xt = to_dev(x, dtype)
+    cent = to_dev(init.astype(np.float32))
+    ties = 0
+    n_ref = torch.zeros(1, dtype=torch.int32, device=dev)
+    heads = range(x.shape[1]) if heads is None else heads
+    for it in range(iters):
+        before = host(cent).astype(np.float64)
+        _, assign, sizes = sva_kmeans(xt, c, 1, cent, n_refined=n_ref)
+        a, sz, after = host(assign), host(sizes), host(cent)
+        for h in heads:
+            xh = x[0, h].astype(np.float64)
+            ref_a, margin = oracle.assign_step(xh, before[0, h])
+            ties += assign_parity(a[0, h], ref_a, margin, f"iter {it} head {h}")
+            assert np.array_equal(sz[0, h], np.bincount(a[0, h], minlength=c))
+            ref_mu, _ = oracle.update_step(xh, a[0, h].astype(np.int64), before[0, h])
+            np.testing.assert_allclose(after[0, h], ref_mu, rtol=2.4e-7, atol=1e-9,
+                                       err_msg=f"iter {it} head {h}")
+    return ties, int(n_ref.item())
+
+
+def test_tiny_config_lockstep_fp32():
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.video_qkv(cfg)
+    for name, c in (("q", cfg.cq), ("k", cfg.ck)):
+        init = synth.gather_init(x[name], synth.kmeans_init_indices(cfg, name, c))
+        ties, _ = _lockstep(x[name], init, c, cfg.iters, torch.float32)
+        assert ties == 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("c", [1, 37, 300])
+def test_small_video_lockstep_bf16(d, c):
+    cfg = synth.CONFIGS["5s"].with_(T=3, heads=2, d=d)      # 4,680 tokens, ragged tile tail
+    x = synth.video_qkv(cfg)["k"]
+    init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "k", c))
+    ties, refined = _lockstep(x, init, c, 4, torch.bfloat16)
+    assert ties <= 2
+
+
+def test_empty_cluster_keeps_centroid_and_c_equals_n():
+    dev = device()
+    rng = np.random.default_rng(0)
+    x = synth.round_bf16(rng.standard_normal((1, 1, 64, 128)).astype(np.float32))
+    init = np.stack([x[0, 0, :5], x[0, 0, :5]]).reshape(1, 1, 10, 128)   # 5 duplicates
+    init[0, 0, 9] = 100.0                                                 # and a far one
+    cent = to_dev(init)
+    _, a, s = sva_kmeans(to_dev(x, torch.bfloat16), 10, 1, cent)
+    s = host(s)[0, 0]
+    assert (s[5:] == 0).all()          # duplicates lose every tie; the far one is empty
+    np.testing.assert_array_equal(host(cent)[0, 0, 5:], init[0, 0, 5:])
+    # c == n with each row its own initial centroid: every row keeps itself
+    cent = to_dev(x.copy())
+    _, a, s = sva_kmeans(to_dev(x, torch.bfloat16), 64, 2, cent)
+    assert np.array_equal(host(a)[0, 0], np.arange(64))
+
+
+def test_chained_ten_iterations_tiny_exact():
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.video_qkv(cfg)
+    for name, c in (("q", cfg.cq), ("k", cfg.ck)):
+        idx = synth.kmeans_init_indices(cfg, name, c)
+        init = synth.gather_init(x[name], idx)
+        cent = to_dev(init)
+        _, a, s = sva_kmeans(to_dev(x[name]), c, cfg.iters, cent)
+        for h in range(cfg.heads):
+            r = oracle.kmeans(x[name][0, h].astype(np.float64), init[0, h].astype(np.float64),
+                              cfg.iters)
+            assert np.array_equal(host(a)[0, h], r.assign)
+            np.testing.assert_allclose(host(cent)[0, h], r.centroids, rtol=1e-6, atol=1e-7)
+
+
+def test_deterministic_bf16():
+    cfg = synth.CONFIGS["5s"].with_(T=2, heads=3)
+    x = synth.video_qkv(cfg)["q"]
+    init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "q", 50))
+    xt = to_dev(x, torch.bfloat16)
+    c1, c2 = to_dev(init), to_dev(init)
+    _, a1, _ = sva_kmeans(xt, 50, 5, c1)
+    _, a2, _ = sva_kmeans(xt, 50, 5, c2)
+    assert torch.equal(a1, a2) and torch.equal(c1, c2)
+
+
+@pytest.fixture(scope="module")
+def video_5s():
+    cfg = synth.CONFIGS["5s"]
+    return cfg, synth.video_qkv(cfg)
+
+
+@pytest.mark.parametrize("name", ["q", "k"])
+def test_full_size_lockstep_two_iterations(video_5s, name):
+    """32,760 tokens x 40 heads, C_q = 100 / C_k = 500, every head checked."""
+    cfg, x = video_5s
+    c = cfg.cq if name == "q" else cfg.ck
+    init = synth.gather_init(x[name], synth.kmeans_init_indices(cfg, name, c))
+    ties, refined = _lockstep(x[name], init, c, 2, torch.bfloat16)
+    print(f"\n{name}: tie mismatches {ties}, rows re-decided in fp64 {refined} "
+          f"({refined / (2 * cfg.heads * cfg.n):.3%})")
+    assert ties <= 10
