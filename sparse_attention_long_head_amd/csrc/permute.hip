@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void sort_hist_rank_kernel(
 
 __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(
     const int32_t *__restrict__ hist, int n, int c, int tiles, int32_t *__restrict__ base,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sizes) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sizes, int32_t *__restrict__ clear) {
   __shared__ int32_t wsum[kScanThreads / 64];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t len = static_cast<size_t>(c) * tiles;
@@ -87,7 +87,13 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(
     if (e % tiles == 0) off[e / tiles] = run;
     run += hh[e];
   }
-  if (tid == 0) off[c] = n;
+  if (tid == 0) {
+    off[c] = n;
+    if (clear != nullptr) {            // per-slice counters of the caller, [2][slices]
+      clear[bh] = 0;
+      clear[gridDim.x + bh] = 0;
+    }
+  }
   if (sizes != nullptr) {
     int32_t *sz = sizes + static_cast<size_t>(bh) * c;
     for (int cl = tid; cl < c; cl += kScanThreads) {
@@ -150,7 +156,7 @@ size_t sort_ws_bytes(int32_t bh, int32_t n, int32_t c) {
 
 hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int32_t c,
                                int32_t *perm, int32_t *offsets, int32_t *sizes, void *ws,
-                               hipStream_t s) {
+                               hipStream_t s, int32_t *clear) {
   const int tiles = (n + kTile - 1) / kTile;
   const size_t hist_bytes = align_up(static_cast<size_t>(bh) * c * tiles * 4, 256);
   int32_t *hist = static_cast<int32_t *>(ws);
@@ -161,7 +167,7 @@ hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sort_scan_kernel, dim3(bh), dim3(kScanThreads), 0, s, hist, n, c, tiles,
-                     base, offsets, sizes);
+                     base, offsets, sizes, clear);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3((n + kThreads - 1) / kThreads, bh),
