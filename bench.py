@@ -89,6 +89,9 @@ def main() -> int:
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run 3 identity-permutation copies of Q (335.5 MB read + "
+                         "335.5 MB written at 5 s) to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -177,6 +180,16 @@ def main() -> int:
                  "frac_of_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                  "speedup_attention_only": dense_ms / attn_ms,
                  "speedup_whole_layer": dense_ms / ms_step}
+
+    if args.copy_calibration:
+        from sparse_attention_long_head_amd import sva_unpermute
+        ident = torch.arange(cfg.n, dtype=torch.int32, device=dev).repeat(
+            cfg.batch * cfg.heads).reshape(cfg.batch, cfg.heads, cfg.n).contiguous()
+        dst = torch.empty_like(t["q"])
+        for _ in range(3):
+            sva_unpermute(t["q"], ident, dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {t['q'].numel() * 2 / 1e6:.1f} MB read + written")
 
     cpu = None
     if not args.no_cpu_baseline:

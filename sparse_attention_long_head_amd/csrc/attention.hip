@@ -14,12 +14,17 @@
 // * The kept K blocks of the Q block form one virtual key sequence (their
 //   row ranges concatenated); it is walked in chunks of 64 keys, so a chunk
 //   may span several small clusters and only the very last chunk is partial.
-//   A chunk's K rows go to LDS row-major (16-byte chunks XOR-swizzled) and its
-//   V rows go to LDS transposed, in the key order the PV MFMA consumes, so
-//   every MFMA operand is one conflict-free ds_read_b128.
-// * Global loads of chunk c+1 are issued before the MFMAs of chunk c and
-//   stored to the other LDS buffer after them: one barrier per chunk.
-// * P is rounded to bf16 for the PV MFMA; max, sum and O accumulate in fp32.
+// * A chunk's K and V rows go from HBM straight to LDS (global_load_lds,
+//   16 bytes per lane, no staging registers), row-major with the 16-byte
+//   pieces XOR-swizzled; each lane picks the global piece that belongs in its
+//   LDS slot.  S^T MFMA operands are conflict-free ds_read_b128 of K; the PV
+//   operand V^T comes from two ds_read_b64_tr_b16 transposing reads, which
+//   hand each lane 4 keys of one d in exactly the key order of P^T.
+// * Loads of chunk c+1 are in flight during the MFMAs of chunk c: one
+//   s_waitcnt + barrier per chunk.
+// * Online softmax with a lazy rescale: the running max only moves (and O is
+//   only rescaled) when a row max exceeds it by more than 2^8, so P <= 256.
+//   P is rounded to bf16 for the PV MFMA; max, sum and O accumulate in fp32.
 // * Work items are laid out so consecutive items of a head run on one XCD
 //   (workgroups are dispatched round-robin over the 8 XCDs), keeping a head's
 //   K/V in that XCD's L2.
@@ -34,25 +39,18 @@
 namespace sva {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kQTile = 128;       // query rows per workgroup
+constexpr int kThreads = 256;       // helper kernels
+constexpr int kAttnThreads = 512;   // bf16 attention: 8 waves
+constexpr int kWaveRows = 32;       // query rows per wave (one 32-row MFMA tile)
+constexpr int kQTile = kWaveRows * (kAttnThreads / 64);   // query rows per workgroup (256)
 constexpr int kKT = 64;           // keys per chunk
 constexpr int kLCap = 1024;       // kept-list entries staged in LDS at a time
-constexpr int kVS = kKT + 8;      // V^T row stride (elements): 144 B, conflict-free
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 struct WorkItem {
   int32_t qb, row0;
 };
-
-// Where chunk-local key k sits inside a V^T row: inside each group of 16 keys,
-// lane half 0 of a PV MFMA consumes keys {0-3, 8-11} and half 1 keys
-// {4-7, 12-15}; storing them as [0-3, 8-11, 4-7, 12-15] makes each half's 8
-// keys contiguous.
-__device__ __forceinline__ int vpos(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
 
 // XOR swizzle of the 16-byte chunks of K row r (rows of 256 B for d=128,
 // 128 B for d=64) so that 16 lanes reading one chunk column hit 16 banks.
@@ -70,8 +68,9 @@ __device__ __forceinline__ int find_block(const int32_t *cum, int segn, int v) {
   return lo;
 }
 
-// In-place exclusive scan of a[0..n) (n <= 4*kThreads) held in LDS; writes
-// the total to a[n].  Must be called by all threads of the workgroup.
+// In-place exclusive scan of a[0..n) (n <= 4*NTHREADS) held in LDS; writes
+// the total to a[n].  Must be called by all NTHREADS threads of the workgroup.
+template <int NTHREADS>
 __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *wsum) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int v[4];
@@ -97,7 +96,7 @@ __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *wsum) {
     if (4 * t + i < n) a[4 * t + i] = run;
     run += v[i];
   }
-  if (t == kThreads - 1) a[n] = run;
+  if (t == NTHREADS - 1) a[n] = run;
   __syncthreads();
 }
 
@@ -160,26 +159,27 @@ __global__ __launch_bounds__(kThreads) void attn_schedule_kernel(const int32_t *
 // bf16 MFMA attention
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, void *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ q_off, const int32_t *__restrict__ k_off,
     const int32_t *__restrict__ kept_count, const int32_t *__restrict__ kept_idx,
     int kept_stride, const WorkItem *__restrict__ work, int work_cap, int n_items, int n_q,
     int n_k, int nqb, int nkb, int dense, float scale_log2) {
-  constexpr int KCH = D / 8;             // 16-byte chunks per row
-  constexpr int KCPT = KCH / 4;          // K chunks loaded per thread (4 threads per key)
-  constexpr int VKPT = kKT * D / 8 / kThreads;   // V keys per thread (4 or 2)
-  constexpr int VGROUPS = kKT / VKPT;    // key groups per chunk (16 or 32)
+  constexpr int PPR = D / 8;             // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;          // rows per 1 KB direct-to-LDS wave load
+  constexpr int LPW = PPR / (kAttnThreads / 64);   // such loads per wave per tensor per chunk
   constexpr int NS = D / 16;             // k-steps of the S MFMA
   constexpr int ND = D / 32;             // d tiles of the O accumulator
+  constexpr int NT = kWaveRows / 32;     // 32-query tiles per wave
+  constexpr float kLazy = 8.f;           // rescale only when a row max grows by > 2^8
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kVS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * D];
   __shared__ int32_t sStart[kLCap];
   __shared__ int32_t sCum[kLCap + 1];
   __shared__ int32_t sRow[2][kKT];
-  __shared__ int32_t sWsum[4];
+  __shared__ int32_t sWsum[kAttnThreads / 64];
 
   int bh, qb, row0;
   if (!decode_work(work, work_cap, n_items, dense, bh, qb, row0)) return;
@@ -188,28 +188,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
   const int h = lane >> 5, col = lane & 31;
   const int qs = dense ? 0 : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb];
   const int qe = dense ? n_q : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb + 1];
-  const int rbase = qs + row0 + wave * 32;
+  const int rbase = qs + row0 + wave * kWaveRows;
   const bool wave_active = rbase < qe;
-  const int myq = rbase + col;
-  const bool qvalid = myq < qe;
+  bool nt_active[NT];
+  int myq[NT];
+  bool qvalid[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    nt_active[nt] = rbase + nt * 32 < qe;      // wave-uniform
+    myq[nt] = rbase + nt * 32 + col;
+    qvalid[nt] = myq[nt] < qe;
+  }
 
-  // Q fragments: lane holds Q[myq][16 s + 8 h .. +8]
-  bf16x8 qf[NS];
-  {
-    const uint16_t *qrow = q + (static_cast<size_t>(bh) * n_q + (qvalid ? myq : 0)) * D + h * 8;
+  // Q fragments: lane holds Q[myq][16 s + 8 h .. +8] (B operand of S^T = K Q^T)
+  bf16x8 qf[NT][NS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint16_t *qrow =
+        q + (static_cast<size_t>(bh) * n_q + (qvalid[nt] ? myq[nt] : 0)) * D + h * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4 raw = qvalid ? *reinterpret_cast<const u32x4 *>(qrow + s * 16) : u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
+      u32x4 raw = qvalid[nt] ? *reinterpret_cast<const u32x4 *>(qrow + s * 16) : u32x4{0, 0, 0, 0};
+      qf[nt][s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
-  f32x16 oacc[ND];
+  f32x16 oacc[NT][ND];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
+  for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[nt][dt][i] = 0.f;
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
 
   const int kc = dense ? 1 : kept_count[static_cast<size_t>(bh) * nqb + qb];
   const int32_t *kidx = kept_idx + (static_cast<size_t>(bh) * nqb + qb) * kept_stride;
@@ -217,15 +231,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
   const uint16_t *kbase = k + static_cast<size_t>(bh) * n_k * D;
   const uint16_t *vbase = v + static_cast<size_t>(bh) * n_k * D;
 
-  // register staging of one chunk
-  u32x4 kreg[KCPT];
-  u32x4 vreg[VKPT];
-  const int kk = tid >> 2, kpart = tid & 3;           // K: key, quarter of the row
-  const int vg = tid % VGROUPS, vdg = tid / VGROUPS;   // V: key group, 8-wide d group
+  // Direct-to-LDS load geometry: wave load j writes LDS bytes [1 KB * (wave*LPW + j), +1 KB):
+  // lane l fills physical piece l % PPR of row RPI*(wave*LPW + j) + l / PPR, i.e. the
+  // logical piece (l % PPR) ^ swizzle(row) of that key row.
+  const int ld_rsub = lane / PPR, ld_piece = lane % PPR;
+
+  // PV operand geometry for ds_read_b64_tr_b16 (4x16 transpose per 16-lane group):
+  // source lane (g, j, q) = (lane/16, (lane/4)%4, lane%4) points at key row
+  // 16 ks + 4 (g/2) + j (+8 for the second read), d = 32 dt + 16 (g%2) + 4 q, so
+  // result lane gets 4 keys of its own d in exactly the key order of the P^T operand.
+  const int tr_g = lane >> 4, tr_j = (lane >> 2) & 3, tr_q = lane & 3;
+  const int tr_row = 4 * (tr_g >> 1) + tr_j;              // + 16 ks (+ 8)
+  const int tr_c0 = 2 * (tr_g & 1) + (tr_q >> 1);         // chunk within a 32-wide d tile
+  const int tr_in = (tr_q & 1) * 4;                        // element within the chunk
+  const int tr_x1 = kswz<D>(tr_row), tr_x2 = kswz<D>(tr_row + 8);
 
   for (int seg0 = 0; seg0 < kc; seg0 += kLCap) {
     const int segn = min(kLCap, kc - seg0);
-    for (int j = tid; j < segn; j += kThreads) {
+    for (int j = tid; j < segn; j += kAttnThreads) {
       int st, len;
       if (dense) {
         st = 0;
@@ -239,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
       sCum[j] = len;
     }
     __syncthreads();
-    block_exclusive_scan(sCum, segn, sWsum);
+    block_exclusive_scan<kAttnThreads>(sCum, segn, sWsum);
     const int L = sCum[segn];
     const int nch = (L + kKT - 1) / kKT;
     if (nch == 0) continue;   // uniform: L is shared
@@ -255,138 +278,141 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         dst[tid] = r;
       }
     };
-    auto issue_loads = [&](const int32_t *rows) {
-      const int r = rows[kk];
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(kbase + static_cast<size_t>(max(r, 0)) * D) +
-                         kpart * KCPT;
+    // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
+    auto issue_loads = [&](const int32_t *rows, int buf) {
+      const int dummy = rows[0];          // always a valid row of this chunk
 #pragma unroll
-      for (int i = 0; i < KCPT; ++i) kreg[i] = (r >= 0) ? src[i] : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < VKPT; ++j) {
-        const int rv = rows[vg * VKPT + j];
-        vreg[j] = (rv >= 0) ? *reinterpret_cast<const u32x4 *>(vbase + static_cast<size_t>(rv) * D +
-                                                                vdg * 8)
-                            : u32x4{0, 0, 0, 0};
-      }
-    };
-    auto store_lds = [&](int buf) {
-      uint16_t *kd = sK[buf] + kk * D;
-#pragma unroll
-      for (int i = 0; i < KCPT; ++i) {
-        const int ch = kpart * KCPT + i;
-        *reinterpret_cast<u32x4 *>(kd + ((ch ^ kswz<D>(kk)) * 8)) = kreg[i];
-      }
-      uint16_t *vd = sV[buf] + vpos(vg * VKPT);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int sh = 16 * (dd & 1);
-        if constexpr (VKPT == 4) {
-          const uint32_t e0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e2 = (vreg[2][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e3 = (vreg[3][dd >> 1] >> sh) & 0xFFFFu;
-          *reinterpret_cast<u32x2 *>(vd + (vdg * 8 + dd) * kVS) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-        } else {
-          const uint32_t e0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
-          *reinterpret_cast<uint32_t *>(vd + (vdg * 8 + dd) * kVS) = e0 | (e1 << 16);
-        }
+      for (int j = 0; j < LPW; ++j) {
+        const int blk = wave * LPW + j;
+        const int r = RPI * blk + ld_rsub;
+        int phys = rows[r];
+        phys = phys < 0 ? dummy : phys;
+        const int off = phys * D + ((ld_piece ^ kswz<D>(r)) << 3);
+        __builtin_amdgcn_global_load_lds(kbase + off,
+                                         (__attribute__((address_space(3))) void *)(sK[buf] + blk * 512),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + off,
+                                         (__attribute__((address_space(3))) void *)(sV[buf] + blk * 512),
+                                         16, 0, 0);
       }
     };
 
     // prologue
     rowmap(0, sRow[0]);
     __syncthreads();
-    issue_loads(sRow[0]);
+    issue_loads(sRow[0], 0);
     if (nch > 1) rowmap(1, sRow[1]);
-    store_lds(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int c = 0; c < nch; ++c) {
       const int buf = c & 1;
-      if (c + 1 < nch) issue_loads(sRow[buf ^ 1]);
+      if (c + 1 < nch) issue_loads(sRow[buf ^ 1], buf ^ 1);
       if (c + 2 < nch) rowmap(c + 2, sRow[buf]);
 
       if (wave_active) {
-        // S^T = K Q^T for 64 keys (two 32-key m-tiles)
-        f32x16 sacc[2];
+        // S^T = K Q^T for 64 keys (two 32-key m-tiles) x the wave's query tiles;
+        // each K fragment is read once per chunk and used by every query tile
         const uint16_t *Kb = sK[buf];
+        f32x16 sacc[NT][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          f32x16 acc;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[i] = 0.f;
           const int r = mt * 32 + col;
+          bf16x8 kf[NS];
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const int ch = 2 * s + h;
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8 *>(Kb + r * D + ((ch ^ kswz<D>(r)) * 8));
-            acc = mfma32x32x16(a, qf[s], acc);
+          for (int s = 0; s < NS; ++s)
+            kf[s] = *reinterpret_cast<const bf16x8 *>(Kb + r * D + (((2 * s + h) ^ kswz<D>(r)) << 3));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[nt][mt][i] = 0.f;
+            if (!nt_active[nt]) continue;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sacc[nt][mt] = mfma32x32x16(kf[s], qf[nt][s], sacc[nt][mt]);
           }
-          sacc[mt] = acc;
         }
-        if ((c + 1) * kKT > L) {     // partial last chunk: mask keys past the end
+        bf16x8 pb[NT][4];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (!nt_active[nt]) continue;
+          if ((c + 1) * kKT > L) {     // partial last chunk: mask keys past the end
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                if (c * kKT + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
+          }
+          float mx = -INFINITY;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (c * kKT + mt * 32 + acc_row(i, h) >= L) sacc[mt][i] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * scale_log2);   // finite: chunk has a key
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float ps = 0.f;
-        bf16x8 pb[4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], scale_log2, -m_new));
-            ps += p;
-            pb[2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[nt][mt][i], sacc[nt][mt][i + 1]));
+          {   // both lane halves hold the same query: exchange with permlane32_swap
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                             __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
           }
-        l_run = l_run * alpha + ps;
-        if (__any(m_new > m_run)) {
+          const float mxs = mx * scale_log2;           // finite: the chunk has a key
+          if (__any(mxs > m_run[nt] + kLazy)) {
+            const float m_new = fmaxf(m_run[nt], mxs);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+            l_run[nt] *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt)
+            for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+              for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+            m_run[nt] = m_new;
+          }
+          float ps = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_run[nt]));
+              ps += p;
+              pb[nt][2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+            }
+          l_run[nt] += ps;
         }
-        m_run = m_new;
-        // O^T += V^T P^T
+        // O^T += V^T P^T; the V operand (transposing reads of row-major V) is
+        // shared by all query tiles
         const uint16_t *Vb = sV[buf];
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8 *>(Vb + (dt * 32 + col) * kVS + ks * 16 + h * 8);
-            oacc[dt] = mfma32x32x16(a, pb[ks], oacc[dt]);
+          for (int dt = 0; dt < ND; ++dt) {
+            const int chunk = (dt << 2) | tr_c0;
+            const uint16_t *p1 = Vb + (ks * 16 + tr_row) * D + ((chunk ^ tr_x1) << 3) + tr_in;
+            const uint16_t *p2 = Vb + (ks * 16 + tr_row + 8) * D + ((chunk ^ tr_x2) << 3) + tr_in;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (bf16x4 __attribute__((address_space(3))) *)(p1));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (bf16x4 __attribute__((address_space(3))) *)(p2));
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              if (nt_active[nt]) oacc[nt][dt] = mfma32x32x16(a, pb[nt][ks], oacc[nt][dt]);
           }
       }
-      if (c + 1 < nch) store_lds(buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   }
 
   // epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qvalid) {
-    const size_t orow = (static_cast<size_t>(bh) * n_q + myq) * D;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (!qvalid[nt]) continue;
+    const size_t orow = (static_cast<size_t>(bh) * n_q + myq[nt]) * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         const int d0 = dt * 32 + 8 * ig + 4 * h;
-        const float o0 = oacc[dt][4 * ig + 0] * inv, o1 = oacc[dt][4 * ig + 1] * inv;
-        const float o2 = oacc[dt][4 * ig + 2] * inv, o3 = oacc[dt][4 * ig + 3] * inv;
+        const float o0 = oacc[nt][dt][4 * ig + 0] * inv, o1 = oacc[nt][dt][4 * ig + 1] * inv;
+        const float o2 = oacc[nt][dt][4 * ig + 2] * inv, o3 = oacc[nt][dt][4 * ig + 3] * inv;
         if constexpr (OUT_F32) {
           *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
         } else {
@@ -395,8 +421,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         }
       }
     if (h == 0 && lse != nullptr)
-      lse[static_cast<size_t>(bh) * n_q + myq] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      lse[static_cast<size_t>(bh) * n_q + myq[nt]] =
+          l_tot > 0.f ? (m_run[nt] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -464,7 +490,7 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
 template <int D, bool OF>
 hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items, int grid,
                     hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, OF>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, OF>), dim3(grid), dim3(kAttnThreads), 0, s,
                      static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                      static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_off, a.k_off,
                      a.kept_count, a.kept_idx, a.kept_stride, work, cap, n_items, a.n_q, a.n_k,
