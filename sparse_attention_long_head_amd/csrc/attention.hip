@@ -16,12 +16,14 @@
 //   may span several small clusters and only the very last chunk is partial.
 // * A chunk's K and V rows go from HBM straight to LDS (global_load_lds,
 //   16 bytes per lane, no staging registers), row-major with the 16-byte
-//   pieces XOR-swizzled; each lane picks the global piece that belongs in its
-//   LDS slot.  S^T MFMA operands are conflict-free ds_read_b128 of K; the PV
-//   operand V^T comes from two ds_read_b64_tr_b16 transposing reads, which
-//   hand each lane 4 keys of one d in exactly the key order of P^T.
-// * Loads of chunk c+1 are in flight during the MFMAs of chunk c: one
-//   s_waitcnt + barrier per chunk.
+//   pieces XOR-swizzled (K and V differently, each for its read pattern);
+//   each lane picks the global piece that belongs in its LDS slot.  S^T MFMA
+//   operands are conflict-free ds_read_b128 of K; the PV operand V^T comes
+//   from two ds_read_b64_tr_b16 transposing reads, which hand each lane 4
+//   keys of one d in exactly the key order of P^T.
+// * Three LDS buffers per tensor: the copies of chunks c+1 and c+2 are in
+//   flight while chunk c is computed; one partial s_waitcnt + one barrier per
+//   chunk.
 // * Online softmax with a lazy rescale: the running max only moves (and O is
 //   only rescaled) when a row max exceeds it by more than 2^8, so P <= 256.
 //   P is rounded to bf16 for the PV MFMA; max, sum and O accumulate in fp32.
@@ -32,6 +34,8 @@
 // The fp32 path is a plain one-thread-per-query kernel (exact fp32, used for
 // small correctness workloads).
 #include <math.h>
+
+#include <type_traits>
 
 #include "../../include/sva.h"
 #include "sva_internal.h"
@@ -44,6 +48,7 @@ constexpr int kAttnThreads = 512;   // bf16 attention: 8 waves
 constexpr int kWaveRows = 32;       // query rows per wave (one 32-row MFMA tile)
 constexpr int kQTile = kWaveRows * (kAttnThreads / 64);   // query rows per workgroup (256)
 constexpr int kKT = 64;           // keys per chunk
+constexpr int kStages = 3;        // K/V chunk buffers in LDS (two chunks in flight)
 constexpr int kLCap = 1024;       // kept-list entries staged in LDS at a time
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -52,11 +57,125 @@ struct WorkItem {
   int32_t qb, row0;
 };
 
-// XOR swizzle of the 16-byte chunks of K row r (rows of 256 B for d=128,
-// 128 B for d=64) so that 16 lanes reading one chunk column hit 16 banks.
+// XOR swizzle of the 16-byte pieces of K row r (rows of 256 B for d=128,
+// 128 B for d=64): the ds_read_b128 of an S^T operand has 16 lanes on 16
+// consecutive rows at one logical piece, which this spreads over all banks.
 template <int D>
-__device__ __forceinline__ int kswz(int r) {
+__host__ __device__ constexpr int kswz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// XOR swizzle of V rows.  A ds_read_b64_tr_b16 of the PV operand has, per 32
+// lanes, 4 consecutive rows x 4 logical pieces x 2 halves; moving row r's
+// pieces by 4 * (r % 4) (d=128) puts the 4 rows in disjoint quarters of the
+// bank space, so the 32 lanes hit 64 distinct banks.  For d=64 two rows share
+// one 256-byte bank line, so the shift follows (r / 2) % 2.
+template <int D>
+__host__ __device__ constexpr int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding (loads
+// complete in issue order).  N < 16; expcnt and lgkmcnt are left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Byte offset of a __shared__ object in the workgroup's LDS (the address the
+// ds_* instructions take).
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+// MFMA operand fragments read from LDS in inline assembly.  The K/V stages are
+// filled by global->LDS copies that stay in flight across the reads of other
+// stages; reads the compiler can see would make it wait for every such copy
+// first (vmcnt(0)), so these reads are kept out of its sight, and the explicit
+// vmcnt wait plus barrier at the top of each step orders them instead.  Each
+// block waits for its own reads before returning (lgkmcnt(0)).
+//
+// K: n = 4 or 8 ds_read_b128, lane address a[s] + OFF.
+template <int OFF, int N>
+__device__ __forceinline__ void lds_read_frags(bf16x8 (&f)[N], const uint32_t (&a)[N]) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  if constexpr (N == 8) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\t"
+        "ds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\t"
+        "ds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\t"
+        "ds_read_b128 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+          "=&v"(f[6]), "=&v"(f[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "i"(OFF)
+        : "memory");
+  } else {
+    static_assert(N == 4, "4 or 8 fragments");
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+        : "memory");
+  }
+}
+
+// V^T: for each of N d tiles two ds_read_b64_tr_b16 (rows +0 and +HI of the
+// k-step) joined into one 8-element operand.
+template <int OFF, int HI, int N>
+__device__ __forceinline__ void lds_read_vt(bf16x8 (&f)[N], const uint32_t (&a)[N]) {
+  static_assert(OFF >= 0 && OFF + HI < 65536, "ds offset field");
+  bf16x4 lo[N], hi[N];
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + HI)
+        : "memory");
+  } else {
+    static_assert(N == 2, "2 or 4 d tiles");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(a[0]), "v"(a[1]), "i"(OFF), "i"(OFF + HI)
+        : "memory");
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) f[i] = __builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Workgroup barrier for LDS only: this wave's LDS accesses complete, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global->LDS copies, which the K/V pipeline keeps in flight across it; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ int find_block(const int32_t *cum, int segn, int v) {
@@ -174,11 +293,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   constexpr int NT = kWaveRows / 32;     // 32-query tiles per wave
   constexpr float kLazy = 8.f;           // rescale only when a row max grows by > 2^8
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * D];
+  constexpr int kStageBytes = kKT * D * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kStages][kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kStages][kKT * D];
   __shared__ int32_t sStart[kLCap];
   __shared__ int32_t sCum[kLCap + 1];
-  __shared__ int32_t sRow[2][kKT];
+  __shared__ int32_t sRow[kStages][kKT];
   __shared__ int32_t sWsum[kAttnThreads / 64];
 
   int bh, qb, row0;
@@ -244,7 +364,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   const int tr_row = 4 * (tr_g >> 1) + tr_j;              // + 16 ks (+ 8)
   const int tr_c0 = 2 * (tr_g & 1) + (tr_q >> 1);         // chunk within a 32-wide d tile
   const int tr_in = (tr_q & 1) * 4;                        // element within the chunk
-  const int tr_x1 = kswz<D>(tr_row), tr_x2 = kswz<D>(tr_row + 8);
+  static_assert(vswz<D>(0) == vswz<D>(8) && vswz<D>(5) == vswz<D>(13), "+8 rows keep the V swizzle");
+  const int tr_x = vswz<D>(tr_row);                        // same for +8 rows and every ks
+
+  // LDS byte addresses of this lane's fragments in stage 0; the stage, m-tile
+  // and k-step offsets are immediates of the reads.  K: piece 2s+h of row col.
+  uint32_t ka[NS], va[ND];
+  const uint32_t sk0 = lds_offset(&sK[0][0]), sv0 = lds_offset(&sV[0][0]);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ka[s] = sk0 + col * D * 2 + (((2 * s + h) ^ kswz<D>(col)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+    va[dt] = sv0 + tr_row * D * 2 + ((((dt << 2) | tr_c0) ^ tr_x) << 4) + tr_in * 2;
 
   for (int seg0 = 0; seg0 < kc; seg0 += kLCap) {
     const int segn = min(kLCap, kc - seg0);
@@ -279,49 +410,61 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       }
     };
     // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
-    auto issue_loads = [&](const int32_t *rows, int buf) {
-      const int dummy = rows[0];          // always a valid row of this chunk
+    auto issue_loads = [&](auto st) {
+      const int32_t *rows = sRow[decltype(st)::value];
+      uint16_t *dk = sK[decltype(st)::value];
+      uint16_t *dv = sV[decltype(st)::value];
+      // past the end of the list (the two chunks after the last) whole stages are
+      // refilled from key row 0, so every step issues the same number of copies
+      const int dummy = max(rows[0], 0);
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int blk = wave * LPW + j;
         const int r = RPI * blk + ld_rsub;
         int phys = rows[r];
         phys = phys < 0 ? dummy : phys;
-        const int off = phys * D + ((ld_piece ^ kswz<D>(r)) << 3);
-        __builtin_amdgcn_global_load_lds(kbase + off,
-                                         (__attribute__((address_space(3))) void *)(sK[buf] + blk * 512),
+        // (offsets stay in named variables: with an arithmetic expression in the
+        // builtin's argument list, hipcc 7.2's host pass emits no launch stub)
+        const int koff = phys * D + ((ld_piece ^ kswz<D>(r)) << 3);
+        const int voff = phys * D + ((ld_piece ^ vswz<D>(r)) << 3);
+        __builtin_amdgcn_global_load_lds(kbase + koff,
+                                         (__attribute__((address_space(3))) void *)(dk + blk * 512),
                                          16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + off,
-                                         (__attribute__((address_space(3))) void *)(sV[buf] + blk * 512),
+        __builtin_amdgcn_global_load_lds(vbase + voff,
+                                         (__attribute__((address_space(3))) void *)(dv + blk * 512),
                                          16, 0, 0);
       }
     };
 
-    // prologue
+    // prologue: chunks 0 and 1 in flight, row map of chunk 2 ready (a row map
+    // past the end of the list is all -1)
     rowmap(0, sRow[0]);
-    __syncthreads();
-    issue_loads(sRow[0], 0);
-    if (nch > 1) rowmap(1, sRow[1]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    rowmap(1, sRow[1]);
+    lds_barrier();
+    issue_loads(std::integral_constant<int, 0>{});
+    issue_loads(std::integral_constant<int, 1>{});
+    rowmap(2, sRow[2]);
 
-    for (int c = 0; c < nch; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < nch) issue_loads(sRow[buf ^ 1], buf ^ 1);
-      if (c + 2 < nch) rowmap(c + 2, sRow[buf]);
+    // chunk c lives in stage c % 3; the body is instantiated per stage
+    auto step = [&](auto st, int c) {
+      constexpr int S = decltype(st)::value;
+      // chunk c has landed once only chunk c+1's copies are outstanding; after
+      // the barrier every wave's copies of chunk c are in LDS and every wave is
+      // done with chunk c-1, whose stage chunk c+2 then refills
+      wait_vmcnt<2 * LPW>();
+      lds_barrier();
+      issue_loads(std::integral_constant<int, (S + 2) % 3>{});
+      rowmap(c + 3, sRow[S]);
 
       if (wave_active) {
         // S^T = K Q^T for 64 keys (two 32-key m-tiles) x the wave's query tiles;
         // each K fragment is read once per chunk and used by every query tile
-        const uint16_t *Kb = sK[buf];
         f32x16 sacc[NT][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int r = mt * 32 + col;
           bf16x8 kf[NS];
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-            kf[s] = *reinterpret_cast<const bf16x8 *>(Kb + r * D + (((2 * s + h) ^ kswz<D>(r)) << 3));
+          if (mt == 0) lds_read_frags<S * kStageBytes>(kf, ka);
+          else lds_read_frags<S * kStageBytes + 32 * D * 2>(kf, ka);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -342,15 +485,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
               for (int i = 0; i < 16; ++i)
                 if (c * kKT + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
           }
+          // (maximum, not maxnum: no NaN canonicalisation, so v_maximum3 does 2 per op)
           float mx = -INFINITY;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[nt][mt][i], sacc[nt][mt][i + 1]));
+            for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sacc[nt][mt][i]);
           {   // both lane halves hold the same query: exchange with permlane32_swap
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
                                                              __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
           }
           const float mxs = mx * scale_log2;           // finite: the chunk has a key
           if (__any(mxs > m_run[nt] + kLazy)) {
@@ -376,27 +520,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
         }
         // O^T += V^T P^T; the V operand (transposing reads of row-major V) is
         // shared by all query tiles
-        const uint16_t *Vb = sV[buf];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 vf[ND];
+          if (ks == 0) lds_read_vt<S * kStageBytes, 8 * D * 2>(vf, va);
+          else if (ks == 1) lds_read_vt<S * kStageBytes + 16 * D * 2, 8 * D * 2>(vf, va);
+          else if (ks == 2) lds_read_vt<S * kStageBytes + 32 * D * 2, 8 * D * 2>(vf, va);
+          else lds_read_vt<S * kStageBytes + 48 * D * 2, 8 * D * 2>(vf, va);
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt) {
-            const int chunk = (dt << 2) | tr_c0;
-            const uint16_t *p1 = Vb + (ks * 16 + tr_row) * D + ((chunk ^ tr_x1) << 3) + tr_in;
-            const uint16_t *p2 = Vb + (ks * 16 + tr_row + 8) * D + ((chunk ^ tr_x2) << 3) + tr_in;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (bf16x4 __attribute__((address_space(3))) *)(p1));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (bf16x4 __attribute__((address_space(3))) *)(p2));
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-              if (nt_active[nt]) oacc[nt][dt] = mfma32x32x16(a, pb[nt][ks], oacc[nt][dt]);
-          }
+              if (nt_active[nt]) oacc[nt][dt] = mfma32x32x16(vf[dt], pb[nt][ks], oacc[nt][dt]);
+        }
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+    };
+    for (int c = 0; c < nch; c += 3) {
+      step(std::integral_constant<int, 0>{}, c);
+      if (c + 1 < nch) step(std::integral_constant<int, 1>{}, c + 1);
+      if (c + 2 < nch) step(std::integral_constant<int, 2>{}, c + 2);
     }
+    wait_vmcnt<0>();   // the copies past the end must land before the stages are reused
+    lds_barrier();     // the next segment reuses the LDS buffers and lists
   }
 
   // epilogue
