@@ -178,15 +178,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int find_block(const int32_t *cum, int segn, int v) {
-  int lo = 0, hi = segn - 1;          // largest j with cum[j] <= v
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cum[mid] <= v) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // In-place exclusive scan of a[0..n) (n <= 4*NTHREADS) held in LDS; writes
 // the total to a[n].  Must be called by all NTHREADS threads of the workgroup.
 template <int NTHREADS>
@@ -299,6 +290,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   __shared__ int32_t sStart[kLCap];
   __shared__ int32_t sCum[kLCap + 1];
   __shared__ int32_t sRow[kStages][kKT];
+  __shared__ int32_t sFlag[kKT];          // row-map scratch, all zero between uses
   __shared__ int32_t sWsum[kAttnThreads / 64];
 
   int bh, qb, row0;
@@ -306,6 +298,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
+  if (tid < kKT) sFlag[tid] = 0;          // ordered before first use by the setup barriers
   const int qs = dense ? 0 : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb];
   const int qe = dense ? n_q : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb + 1];
   const int rbase = qs + row0 + wave * kWaveRows;
@@ -378,35 +371,65 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     va[dt] = sv0 + tr_row * D * 2 + ((((dt << 2) | tr_c0) ^ tr_x) << 4) + tr_in * 2;
 
   for (int seg0 = 0; seg0 < kc; seg0 += kLCap) {
+    // the segment's kept clusters as key-row ranges, empty ones dropped:
+    // sStart[j] = first row, sCum[j] = virtual index of that row (exclusive scan)
     const int segn = min(kLCap, kc - seg0);
-    for (int j = tid; j < segn; j += kAttnThreads) {
-      int st, len;
-      if (dense) {
-        st = 0;
-        len = n_k;
-      } else {
-        const int b = kidx[seg0 + j];
-        st = koff[b];
-        len = koff[b + 1] - st;
+    static_assert(kLCap == 2 * kAttnThreads, "two list entries per thread");
+    int st_r[2], len_r[2], ci[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = tid + u * kAttnThreads;
+      st_r[u] = 0;
+      len_r[u] = 0;
+      if (j < segn) {
+        if (dense) {
+          len_r[u] = n_k;
+        } else {
+          const int b = kidx[seg0 + j];
+          st_r[u] = koff[b];
+          len_r[u] = koff[b + 1] - st_r[u];
+        }
       }
-      sStart[j] = st;
-      sCum[j] = len;
+      sCum[j] = len_r[u] > 0 ? 1 : 0;
     }
     __syncthreads();
     block_exclusive_scan<kAttnThreads>(sCum, segn, sWsum);
-    const int L = sCum[segn];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ci[u] = sCum[tid + u * kAttnThreads];
+    const int nseg = sCum[segn];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (len_r[u] > 0) {
+        sStart[ci[u]] = st_r[u];
+        sCum[ci[u]] = len_r[u];
+      }
+    __syncthreads();
+    block_exclusive_scan<kAttnThreads>(sCum, nseg, sWsum);
+    const int L = sCum[nseg];
     const int nch = (L + kKT - 1) / kKT;
     if (nch == 0) continue;   // uniform: L is shared
 
+    // Row map of chunk c (wave 0; chunks are mapped in order 0, 1, 2, ...):
+    // jcur is the range holding the chunk's first key.  Ranges are non-empty,
+    // so only the next 64 range starts can fall in the chunk or at the start
+    // of the next one; lane i takes start jcur+1+i.  Each start inside the
+    // chunk marks its position, and a ballot of the marks gives every lane the
+    // number of range starts at or before its key, hence its range.
+    int jcur = 0;
     auto rowmap = [&](int c, int32_t *dst) {
-      if (tid < kKT) {
-        const int vv = c * kKT + tid;
-        int r = -1;
-        if (vv < L) {
-          const int j = find_block(sCum, segn, vv);
-          r = sStart[j] + (vv - sCum[j]);
-        }
-        dst[tid] = r;
+      if (wave == 0) {
+        const int c0 = c * kKT;
+        const int jb = jcur + 1 + lane;
+        const int p = (jb <= nseg ? sCum[jb] : INT_MAX - kKT) - c0;   // >= 1; sCum[nseg] = L
+        const bool mark = p < kKT;
+        if (mark) sFlag[p] = 1;
+        const uint64_t starts = __ballot(sFlag[lane] != 0);
+        if (mark) sFlag[p] = 0;
+        const int seg = jcur + __popcll(starts & ((2ull << lane) - 1));
+        const int vv = c0 + lane;
+        dst[lane] = vv < L ? sStart[seg] + (vv - sCum[seg]) : -1;
+        jcur += __popcll(__ballot(p <= kKT));     // the range holding key c0 + 64
       }
     };
     // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
@@ -440,10 +463,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     // past the end of the list is all -1)
     rowmap(0, sRow[0]);
     rowmap(1, sRow[1]);
+    rowmap(2, sRow[2]);
     lds_barrier();
     issue_loads(std::integral_constant<int, 0>{});
     issue_loads(std::integral_constant<int, 1>{});
-    rowmap(2, sRow[2]);
 
     // chunk c lives in stage c % 3; the body is instantiated per stage
     auto step = [&](auto st, int c) {

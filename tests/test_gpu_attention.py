@@ -128,6 +128,39 @@ def test_variable_blocks(bf16, seed):
         check_lse(lse[0, h], rl, 1e-3 if bf16 else 1e-5)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_one_key_blocks_and_empty_blocks(bf16):
+    # every kept key block holds one key or none: a 64-key chunk then spans 64
+    # key blocks (the most it can), with empty blocks interleaved in the list
+    rng = np.random.default_rng(9)
+    d, nq, nk = 64, 150, 333
+    sizes = np.ones(300, np.int32)
+    sizes[3::7] = 0                                  # empty blocks in between
+    sizes[-1] = nk - sizes[:-1].sum()                # one large block at the end
+    koff = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)[None, None]
+    nkb = sizes.size
+    dt = "bf16" if bf16 else "f32"
+    q = rand_inputs((1, 1, nq, d), 60, dt)
+    k = rand_inputs((1, 1, nk, d), 61, dt)
+    v = rand_inputs((1, 1, nk, d), 62, dt)
+    qoff = np.array([[[0, 70, nq]]], np.int32)
+    masks = np.ones((1, 1, 2, nkb), bool)
+    masks[0, 0, 1] = rng.random(nkb) < 0.6
+    cnt, idx = synth.mask_to_ell(masks)
+    T = _tdtype(bf16)
+    scale = 1 / math.sqrt(d)
+    o, lse = sva_block_sparse_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T),
+                                   to_dev(qoff, torch.int32), to_dev(koff, torch.int32),
+                                   to_dev(cnt, torch.int32), to_dev(idx, torch.int32), scale,
+                                   want_lse=True)
+    aq = np.repeat(np.arange(2), np.diff(qoff[0, 0]))
+    ak = np.repeat(np.arange(nkb), sizes)
+    ro, rl = oracle.cluster_sparse_attention(q[0, 0], k[0, 0], v[0, 0], aq, ak, masks[0, 0],
+                                             np.float32(scale))
+    check_attention(host(o)[0, 0], ro, bf16)
+    check_lse(host(lse)[0, 0], rl, 1e-3 if bf16 else 1e-5)
+
+
 def test_kept_list_longer_than_one_lds_segment():
     # 1300 two-key blocks, all kept: the kept list is walked in several segments
     rng = np.random.default_rng(5)
