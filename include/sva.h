@@ -96,7 +96,9 @@ int32_t sva_kmeans(const void *x, int32_t dtype, int32_t batch, int32_t heads, i
  * A stable counting sort of the rows of each slice by cluster id: clusters in
  * ascending id, rows of a cluster in ascending original index.
  *
- *   assign     [bh][n] int32, values in [0, c) (device precondition)
+ *   assign     [bh][n] int32 cluster ids in [0, c); an id outside that range
+ *              is clamped into it on the device (no error is reported, and
+ *              no memory outside the arguments is touched)
  *   perm       [bh][n] int32 OUT: perm[i] = original row of permuted row i
  *   offsets    [bh][c+1] int32 OUT: cluster j is permuted rows
  *              [offsets[j], offsets[j+1]); offsets[c] = n

@@ -14,7 +14,9 @@
 //   error bound E (split residual + fp32 accumulation of 2d exact products and
 //   the start value + final rounding, from ||x|| and max ||c||).  A row whose
 //   best two w are more than 2E apart is decided; any other row is queued
-//   with the threshold best - 2E.
+//   with the threshold best - 2E (each token tile writes its queued rows to a
+//   region of its own; a join kernel concatenates the regions in tile order,
+//   so there are no atomics and the queue order is deterministic).
 // refine: queued rows run through the same MFMA loop; every cluster with
 //   w >= threshold (a set that provably holds the true argmin) goes to an LDS
 //   candidate list; one wave per candidate computes the exact fp64 distance,
@@ -22,12 +24,13 @@
 //   therefore equal exact-arithmetic ones.
 // assign (fp32 inputs): plain fp64 distances for every cluster.
 // sort: the counting sort of permute.hip gives every cluster's rows in
-//   ascending token order (and clears the per-slice counters for the next
+//   ascending token order (and clears the per-slice queue lengths for the next
 //   iteration).
-// mean: one workgroup per cluster sums its rows in that fixed order in fp64
-//   and rounds the mean to fp32 once, so results are deterministic; an empty
-//   cluster keeps its centroid.  The same kernel splits the new centroids
-//   into hi/lo bf16 and computes -||c||^2/2 and max ||c|| for the next assign.
+// mean: one wave (small clusters) or four (large ones) per cluster sum its
+//   rows in that fixed order in fp64 and round the mean to fp32 once, so
+//   results are deterministic; an empty cluster keeps its centroid.  The same kernel splits the new centroids
+//   into hi/lo bf16 and computes -||c||^2/2 for the next assign (whose
+//   workgroups take max ||c|| of their slice from it).
 #include <math.h>
 
 #include "../../include/sva.h"
@@ -47,10 +50,10 @@ __device__ __forceinline__ int cswz(int r) {
 }
 
 struct KmLayout {
-  size_t chi, clo, nh, ctl, flags, perm, offsets, sort, total;
+  size_t chi, clo, nh, ctl, flags, tflags, tcount, perm, offsets, sort, total;
 };
 
-// ctl holds 2*bh ints: queue counters [0, bh) and max-norm bits [bh, 2bh)
+// ctl holds the bh refine-queue lengths
 KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   const size_t cpad = (static_cast<size_t>(c) + 31) / 32 * 32;
   KmLayout L{};
@@ -63,8 +66,10 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   L.chi = take(static_cast<size_t>(bh) * cpad * d * 2);
   L.clo = take(static_cast<size_t>(bh) * cpad * d * 2);
   L.nh = take(static_cast<size_t>(bh) * cpad * 4);
-  L.ctl = take(static_cast<size_t>(bh) * 2 * 4);
+  L.ctl = take(static_cast<size_t>(bh) * 4);
   L.flags = take(static_cast<size_t>(bh) * n * 8);
+  L.tflags = take(static_cast<size_t>(bh) * n * 8);
+  L.tcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
   L.perm = take(static_cast<size_t>(bh) * n * 4);
   L.offsets = take(static_cast<size_t>(bh) * (c + 1) * 4);
   L.sort = take(sort_ws_bytes(bh, n, c));
@@ -80,13 +85,16 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
     const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
     const uint16_t *__restrict__ clo, const float *__restrict__ nh,
     const int32_t *__restrict__ ctl, const float *__restrict__ cent,
-    int32_t *__restrict__ assign, int2 *__restrict__ flags, int32_t *__restrict__ qcount,
-    int32_t *__restrict__ n_refined, int nbh, int tph) {
+    int32_t *__restrict__ assign, int2 *__restrict__ flags, int2 *__restrict__ tflags,
+    int32_t *__restrict__ tcount, int32_t *__restrict__ n_refined, int nbh, int tph) {
   constexpr int NS = D / 16;
   constexpr int KCH = D / 8;                 // 16-byte chunks per centroid row
   constexpr int CPT = KCH / 4;               // chunks per thread per tile load
   constexpr int CC = REFINE ? kCandCap : 1;
-  constexpr int TS = REFINE ? kTokTile : 1;
+  // the refine pass takes 32 queued rows per wave: more workgroups share a queue
+  constexpr int NT = REFINE ? 1 : kNT;
+  constexpr int TOKT = NT * 32 * (kThreads / 64);
+  constexpr int TS = REFINE ? TOKT : 1;
   __shared__ __attribute__((aligned(16))) uint16_t sC[2][2][32 * D];
   __shared__ __attribute__((aligned(16))) float sN[2][32];
   __shared__ int32_t s_cand[CC];
@@ -96,6 +104,8 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
   __shared__ int32_t s_tok[TS];
   __shared__ int32_t s_over[TS];
   __shared__ int32_t s_ncand;
+  __shared__ int32_t s_wq[kThreads / 64];
+  __shared__ float s_nhmin[kThreads / 64];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; slices are dealt
   // to XCDs the same way, so all tiles of a slice run on one XCD and its
@@ -109,8 +119,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
   const int ntl = cpad / 32;
   const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
   const int ntok = REFINE ? ctl[bh] : n;
-  const float cm = __int_as_float(ctl[nbh + bh]);
-  const int step = tph * kTokTile;
+  const int step = tph * TOKT;
 
   // tile loader: thread -> (split, row, quarter of the row)
   const int ld_split = tid >> 7, ld_row = (tid >> 2) & 31, ld_part = tid & 3;
@@ -135,14 +144,14 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
   };
 
   // main pass: one tile of tokens per workgroup; refine: grid-stride over the queue
-  for (int base = tile * kTokTile; base < ntok; base = REFINE ? base + step : ntok) {
-    int tok[kNT];
-    bool tv[kNT];
-    float thr[kNT];
-    bf16x8 xf[kNT][NS];
+  for (int base = tile * TOKT; base < ntok; base = REFINE ? base + step : ntok) {
+    int tok[NT];
+    bool tv[NT];
+    float thr[NT];
+    bf16x8 xf[NT][NS];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const int slot = wave * (kNT * 32) + nt * 32 + col;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int slot = wave * (NT * 32) + nt * 32 + col;
       const int idx = base + slot;
       tv[nt] = idx < ntok;
       tok[nt] = idx;
@@ -170,11 +179,11 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
     if constexpr (REFINE) {
       if (tid == 0) s_ncand = 0;
     }
-    // error bound of w per token: 2E (main pass)
-    float two_e[kNT];
+    // ||x|| bound per token (main pass), for the error bound of w
+    float nx[NT];
     if constexpr (!REFINE) {
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         float p = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -184,17 +193,21 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
             p = fmaf(f, f, p);
           }
         p += __shfl_xor(p, 32);
-        const float nx = sqrtf(p) * (1.f + 0x1p-10f);
-        const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx * cm +
-                        (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx * cm);
-        two_e[nt] = 2.f * 1.25f * e;
+        nx[nt] = sqrtf(p) * (1.f + 0x1p-10f);
       }
+      // max ||c|| of the slice from -||c||^2/2 of its real clusters (the
+      // per-wave minima are read after the first barrier below)
+      float mn = 0.f;
+      for (int j = tid; j < c; j += kThreads) mn = fminf(mn, nh[static_cast<size_t>(bh) * cpad + j]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
+      if (lane == 0) s_nhmin[wave] = mn;
     }
 
-    float b1[kNT], b2[kNT];
-    int i1[kNT];
+    float b1[NT], b2[NT];
+    int i1[NT];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       b1[nt] = -INFINITY;
       b2[nt] = -INFINITY;
       i1[nt] = 0;
@@ -213,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) cinit[4 * g + j] = q4[j];
       }
-      f32x16 acc[kNT];
+      f32x16 acc[NT];
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
@@ -221,11 +234,11 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
           const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
               sC[buf][sp] + col * D + (((2 * s + h) ^ cswz<D>(col)) * 8));
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
             acc[nt] = mfma32x32x16(a, xf[nt][s], (sp == 0 && s == 0) ? cinit : acc[nt]);
         }
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int cl = ct * 32 + acc_row(i, h);
@@ -237,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
             i1[nt] = gt ? cl : i1[nt];
           } else {
             if (tv[nt] && cl < c && w >= thr[nt]) {
-              const int slot = wave * (kNT * 32) + nt * 32 + col;
+              const int slot = wave * (NT * 32) + nt * 32 + col;
               const int k = atomicAdd(&s_ncand, 1);
               if (k < kCandCap) s_cand[k] = (slot << 14) | cl;
               else s_over[slot] = 1;
@@ -249,23 +262,58 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
     }
 
     if constexpr (!REFINE) {
+      // error bound E of every w of a token (split residual of the centroid,
+      // fp32 accumulation of 2d exact products and the start value, final
+      // rounding), from ||x|| and the slice's max ||c|| (with margin)
+      float nhmin = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
+      for (int w = 0; w < kThreads / 64; ++w) nhmin = fminf(nhmin, s_nhmin[w]);
+      const float cm = sqrtf(-2.f * nhmin) * (1.f + 0x1p-20f);
+      float two_e[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx[nt] * cm +
+                        (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx[nt] * cm);
+        two_e[nt] = 2.f * 1.25f * e;
+      }
+      // decided rows are assigned; the others are compacted, in wave and lane
+      // order, into this tile's region of the slice's queue area (tflags), with
+      // their count in tcount; a compaction kernel then joins the regions
+      bool queued[NT];
+      uint64_t qm[NT];
+      int ival[NT], thr_bits[NT];
+      int wq = 0;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
         const float ob1 = __shfl_xor(b1[nt], 32), ob2 = __shfl_xor(b2[nt], 32);
         const int oi1 = __shfl_xor(i1[nt], 32);
         const bool other = ob1 > b1[nt] || (ob1 == b1[nt] && oi1 < i1[nt]);
         const float nb1 = fmaxf(b1[nt], ob1);
-        const int ni1 = other ? oi1 : i1[nt];
+        ival[nt] = other ? oi1 : i1[nt];
         const float nb2 = fmaxf(fminf(b1[nt], ob1), fmaxf(b2[nt], ob2));
-        if (h == 0 && tv[nt]) {
-          if (nb1 - nb2 > two_e[nt]) {
-            assign[static_cast<size_t>(bh) * n + tok[nt]] = ni1;
-          } else {
-            const int q = atomicAdd(&qcount[bh], 1);
-            flags[static_cast<size_t>(bh) * n + q] = int2{tok[nt], __float_as_int(nb1 - two_e[nt])};
-          }
-        }
+        const bool decided = nb1 - nb2 > two_e[nt];
+        if (h == 0 && tv[nt] && decided) assign[static_cast<size_t>(bh) * n + tok[nt]] = ival[nt];
+        queued[nt] = h == 0 && tv[nt] && !decided;
+        thr_bits[nt] = __float_as_int(nb1 - two_e[nt]);
+        qm[nt] = __ballot(queued[nt]);
+        wq += __popcll(qm[nt]);
       }
+      if (lane == 0) s_wq[wave] = wq;
+      __syncthreads();
+      int q = tile * TOKT, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) {
+        q += w < wave ? s_wq[w] : 0;
+        tot += s_wq[w];
+      }
+      const uint64_t lt = (1ull << lane) - 1;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (queued[nt])
+          tflags[static_cast<size_t>(bh) * n + q + __popcll(qm[nt] & lt)] = int2{tok[nt], thr_bits[nt]};
+        q += __popcll(qm[nt]);
+      }
+      if (tid == 0) tcount[static_cast<size_t>(bh) * tph + tile] = tot;
     } else {
       // exact fp64 distance of every candidate, one lane per candidate (rows read
       // as 16-byte pieces, summed in ascending dimension order)
@@ -300,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
       }
       __syncthreads();
       int done = 0;
-      for (int slot = tid; slot < kTokTile; slot += kThreads) {
+      for (int slot = tid; slot < TOKT; slot += kThreads) {
         const int t = s_tok[slot];
         if (t < 0) continue;
         int best = s_bestc[slot];
@@ -329,6 +377,51 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
       __syncthreads();
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// refine queue of a slice: the per-tile regions of tflags joined in tile order
+// into flags[0, total); total goes to qcount[slice].  One workgroup per slice.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void km_queue_join_kernel(
+    const int2 *__restrict__ tflags, const int32_t *__restrict__ tcount, int n, int tph,
+    int2 *__restrict__ flags, int32_t *__restrict__ qcount) {
+  __shared__ int32_t s_cnt[kThreads];
+  __shared__ int32_t s_pre[kThreads];
+  __shared__ int32_t s_w[kThreads / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int2 *src = tflags + static_cast<size_t>(bh) * n;
+  int2 *dst = flags + static_cast<size_t>(bh) * n;
+  int base = 0;
+  for (int t0 = 0; t0 < tph; t0 += kThreads) {
+    const int cnt = t0 + tid < tph ? tcount[static_cast<size_t>(bh) * tph + t0 + tid] : 0;
+    int x = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_w[wave] = x;
+    s_cnt[tid] = cnt;
+    __syncthreads();
+    int pre = x - cnt, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      pre += w < wave ? s_w[w] : 0;
+      tot += s_w[w];
+    }
+    s_pre[tid] = base + pre;
+    __syncthreads();
+    // one wave per tile region, lanes over its entries
+    for (int t = wave; t < kThreads && t0 + t < tph; t += kThreads / 64) {
+      const int c = s_cnt[t], o = s_pre[t];
+      const int2 *from = src + static_cast<size_t>(t0 + t) * kTokTile;
+      for (int j = lane; j < c; j += 64) dst[o + j] = from[j];
+    }
+    base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) qcount[bh] = base;
 }
 
 // ---------------------------------------------------------------------------
@@ -374,89 +467,132 @@ __global__ __launch_bounds__(kThreads) void km_assign_f64_kernel(const float *__
 // ---------------------------------------------------------------------------
 // mean of every cluster in fixed (ascending token) order + next-assign prep
 //   mode 0: prep only (initial centroids); 1: mean + prep; 2: mean only
+// WPC waves per cluster (1: four clusters per workgroup, for small clusters;
+// 4: one cluster per workgroup, for large ones).  The cluster's rows are taken
+// in batches of 64; wave w of the cluster takes batches w, w+WPC, ...  A row is
+// read as TPR 16-byte pieces (one per lane) and lane group g of a wave takes
+// rows g, g+RG, ... of each batch.  Each lane sums its rows in ascending
+// order in fp64; lane groups and then waves are added in a fixed order, so
+// the result does not depend on scheduling.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void km_mean_kernel(
+constexpr int kMeanWaves = 4;
+
+template <int D, bool BF16, int WPC>
+__global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
     const void *__restrict__ x, int n, int c, int cpad, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, float *__restrict__ cent, uint16_t *__restrict__ chi,
-    uint16_t *__restrict__ clo, float *__restrict__ nh, int32_t *__restrict__ cmax, int mode) {
+    uint16_t *__restrict__ clo, float *__restrict__ nh, int mode, int ncl) {
   constexpr int EB = BF16 ? 2 : 4;           // element bytes
   constexpr int EPT = 16 / EB;               // elements per 16-byte piece
-  constexpr int TPR = D / EPT;               // threads per row
-  constexpr int RG = kThreads / TPR;         // row groups
-  constexpr int U = 8;                       // rows in flight per thread
-  __shared__ double part[RG * D];
-  __shared__ double red[kThreads / 64];
-  const int cl = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  constexpr int TPR = D / EPT;               // lanes per row
+  constexpr int RG = 64 / TPR;               // row groups per wave
+  constexpr int U = (64 / RG) < 16 ? (64 / RG) : 16;   // rows in flight per lane
+  static_assert(TPR <= 64 && 64 % TPR == 0 && (64 / RG) % U == 0, "row layout");
+  static_assert(WPC == 1 || WPC == kMeanWaves, "waves per cluster");
+  __shared__ double s_part[WPC > 1 ? WPC : 1][WPC > 1 ? D : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wc = WPC > 1 ? wave : 0;         // this wave's rank within its cluster
+  const int cl = WPC > 1 ? blockIdx.x : blockIdx.x * kMeanWaves + wave, bh = blockIdx.y;
+  if (cl >= ncl) return;                     // uniform over the cluster's waves
   const bool real = cl < c;
-  float val = 0.f;   // this thread's coordinate (tid < D) of the final centroid
-  if (real && tid < D) val = cent[(static_cast<size_t>(bh) * c + cl) * D + tid];
+  const int g = lane / TPR, pc = lane % TPR;
+  float val[EPT];                            // coordinates pc*EPT.. of the final centroid
+  const size_t crow = (static_cast<size_t>(bh) * c + cl) * D + pc * EPT;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) val[e] = real ? cent[crow + e] : 0.f;
   if (mode != 0 && real) {
     const int st = offsets[static_cast<size_t>(bh) * (c + 1) + cl];
     const int en = offsets[static_cast<size_t>(bh) * (c + 1) + cl + 1];
-    const int rg = tid / TPR, pc = tid % TPR;
-    double acc[EPT];
+    if (en > st) {                           // uniform over the cluster's waves
+      double acc[EPT];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
-    const int32_t *pm = perm + static_cast<size_t>(bh) * n;
-    const char *xb = static_cast<const char *>(x) + static_cast<size_t>(bh) * n * D * EB;
-    for (int r0 = st + rg; r0 < en; r0 += U * RG) {
-      int pr[U];
+      for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
+      const int32_t *pm = perm + static_cast<size_t>(bh) * n;
+      const char *xb = static_cast<const char *>(x) + static_cast<size_t>(bh) * n * D * EB;
+      // lane j fetches the index of row r0 + j (the next batch's indices load
+      // while this batch's rows are summed)
+      int r0 = st + 64 * wc;
+      int pidx = r0 + lane < en ? pm[r0 + lane] : -1;
+      for (; r0 < en; r0 += 64 * WPC) {
+        const int cur = pidx;
+        const int rn = r0 + 64 * WPC + lane;
+        pidx = rn < en ? pm[rn] : -1;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * RG;
-        pr[u] = r < en ? pm[r] : -1;
-      }
-      u32x4 buf[U];
+        for (int sb = 0; sb < 64 / RG; sb += U) {
+          int pr[U];
+          u32x4 buf[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        buf[u] = pr[u] >= 0 ? *reinterpret_cast<const u32x4 *>(
-                                  xb + (static_cast<size_t>(pr[u]) * D + pc * EPT) * EB)
-                            : u32x4{0, 0, 0, 0};
+          for (int u = 0; u < U; ++u) {
+            pr[u] = __shfl(cur, g + RG * (sb + u));
+            buf[u] = pr[u] >= 0 ? *reinterpret_cast<const u32x4 *>(
+                                      xb + (static_cast<size_t>(pr[u]) * D + pc * EPT) * EB)
+                                : u32x4{0, 0, 0, 0};
+          }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (pr[u] < 0) break;
+          for (int u = 0; u < U; ++u) {
+            if (pr[u] < 0) continue;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          float f;
-          if constexpr (BF16) f = bf16_bits_to_f32(static_cast<uint16_t>(buf[u][e >> 1] >> (16 * (e & 1))));
-          else f = __uint_as_float(buf[u][e]);
-          acc[e] += static_cast<double>(f);
+            for (int e = 0; e < EPT; ++e) {
+              float f;
+              if constexpr (BF16) f = bf16_bits_to_f32(static_cast<uint16_t>(buf[u][e >> 1] >> (16 * (e & 1))));
+              else f = __uint_as_float(buf[u][e]);
+              acc[e] += static_cast<double>(f);
+            }
+          }
         }
       }
-    }
+      // combine the row groups (lanes TPR apart), then the cluster's waves
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) part[rg * D + pc * EPT + e] = acc[e];
-    __syncthreads();
-    if (tid < D && en > st) {
-      double s = 0.0;
-      for (int g = 0; g < RG; ++g) s += part[g * D + tid];
-      val = static_cast<float>(s / static_cast<double>(en - st));
-      cent[(static_cast<size_t>(bh) * c + cl) * D + tid] = val;
+      for (int off = TPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc[e] += __shfl_xor(acc[e], off);
+      if constexpr (WPC > 1) {
+        if (g == 0) {
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) s_part[wc][pc * EPT + e] = acc[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          double t = s_part[0][pc * EPT + e];
+#pragma unroll
+          for (int w = 1; w < WPC; ++w) t += s_part[w][pc * EPT + e];
+          acc[e] = t;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) val[e] = static_cast<float>(acc[e] / static_cast<double>(en - st));
+      if (g == 0 && wc == 0) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) cent[crow + e] = val[e];
+      }
     }
   }
-  if (mode == 2) return;
-  // prep for the next assignment: hi/lo split, -||c||^2/2, max ||c||
+  if (mode == 2 || wc != 0) return;
+  // prep for the next assignment (first wave of the cluster): hi/lo split,
+  // -||c||^2/2
   double sq = 0.0;
-  if (tid < D) {
-    const __bf16 hi = static_cast<__bf16>(val);
-    const __bf16 lo = static_cast<__bf16>(val - static_cast<float>(hi));
-    const size_t o = (static_cast<size_t>(bh) * cpad + cl) * D + tid;
-    chi[o] = __builtin_bit_cast(uint16_t, hi);
-    clo[o] = __builtin_bit_cast(uint16_t, lo);
-    sq = static_cast<double>(val) * static_cast<double>(val);
+  if (g == 0) {
+    uint16_t hb[EPT], lb[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const __bf16 hi = static_cast<__bf16>(val[e]);
+      const __bf16 lo = static_cast<__bf16>(val[e] - static_cast<float>(hi));
+      hb[e] = __builtin_bit_cast(uint16_t, hi);
+      lb[e] = __builtin_bit_cast(uint16_t, lo);
+      sq += static_cast<double>(val[e]) * static_cast<double>(val[e]);
+    }
+    const size_t o = (static_cast<size_t>(bh) * cpad + cl) * D + pc * EPT;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      chi[o + e] = hb[e];
+      clo[o + e] = lb[e];
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-  if ((tid & 63) == 0) red[tid >> 6] = sq;
-  __syncthreads();
-  if (tid == 0) {
-    double ss = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) ss += red[w];
-    nh[static_cast<size_t>(bh) * cpad + cl] = real ? static_cast<float>(-0.5 * ss) : -INFINITY;
-    if (real)
-      atomicMax(&cmax[bh], __float_as_int(static_cast<float>(sqrt(ss)) * (1.f + 0x1p-20f)));
-  }
+  if (lane == 0)
+    nh[static_cast<size_t>(bh) * cpad + cl] = real ? static_cast<float>(-0.5 * sq) : -INFINITY;
 }
 
 template <int D>
@@ -466,8 +602,10 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   uint16_t *chi = reinterpret_cast<uint16_t *>(w + L.chi);
   uint16_t *clo = reinterpret_cast<uint16_t *>(w + L.clo);
   float *nh = reinterpret_cast<float *>(w + L.nh);
-  int32_t *ctl = reinterpret_cast<int32_t *>(w + L.ctl);   // [bh] queue counts, [bh] max norms
+  int32_t *ctl = reinterpret_cast<int32_t *>(w + L.ctl);   // [bh] refine-queue lengths
   int2 *flags = reinterpret_cast<int2 *>(w + L.flags);
+  int2 *tflags = reinterpret_cast<int2 *>(w + L.tflags);
+  int32_t *tcount = reinterpret_cast<int32_t *>(w + L.tcount);
   int32_t *perm = reinterpret_cast<int32_t *>(w + L.perm);
   int32_t *offsets = reinterpret_cast<int32_t *>(w + L.offsets);
   void *sort_ws = w + L.sort;
@@ -482,19 +620,28 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e; \
   } while (0)
 
+  // clusters of 256 rows or more on average get four waves each
+  const bool wide = a.n >= 256LL * a.c;
   auto mean = [&](int mode) -> hipError_t {
-    const dim3 grid(mode == 2 ? a.c : cpad, a.bh);
-    if (bf16)
-      hipLaunchKernelGGL((km_mean_kernel<D, true>), grid, dim3(kThreads), 0, s, a.x, a.n, a.c,
-                         cpad, perm, offsets, a.centroids, chi, clo, nh, ctl + a.bh, mode);
-    else
-      hipLaunchKernelGGL((km_mean_kernel<D, false>), grid, dim3(kThreads), 0, s, a.x, a.n, a.c,
-                         cpad, perm, offsets, a.centroids, chi, clo, nh, ctl + a.bh, mode);
+    const int ncl = mode == 2 ? a.c : cpad;
+    const dim3 grid(wide ? ncl : (ncl + kMeanWaves - 1) / kMeanWaves, a.bh);
+    const dim3 block(64 * kMeanWaves);
+#define SVA_MEAN(B, W)                                                                       \
+  hipLaunchKernelGGL((km_mean_kernel<D, B, W>), grid, block, 0, s, a.x, a.n, a.c, cpad, perm, \
+                     offsets, a.centroids, chi, clo, nh, mode, ncl)
+    if (bf16) {
+      if (wide) SVA_MEAN(true, kMeanWaves);
+      else SVA_MEAN(true, 1);
+    } else {
+      if (wide) SVA_MEAN(false, kMeanWaves);
+      else SVA_MEAN(false, 1);
+    }
+#undef SVA_MEAN
     return hipGetLastError();
   };
 
   if (bf16) {
-    SVA_CHECK(launch_fill_i32(ctl, 0, 2 * static_cast<size_t>(a.bh), s));
+    SVA_CHECK(launch_fill_i32(ctl, 0, static_cast<size_t>(a.bh), s));
     SVA_CHECK(mean(0));
   }
   for (int it = 0; it < a.iters; ++it) {
@@ -502,11 +649,14 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     if (bf16) {
       hipLaunchKernelGGL((km_assign_mfma_kernel<D, false>), tok_grid, dim3(kThreads), 0, s,
                          static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, ctl,
-                         a.centroids, a.assign, flags, ctl, a.n_refined, a.bh, tph);
+                         a.centroids, a.assign, flags, tflags, tcount, a.n_refined, a.bh, tph);
+      SVA_CHECK(hipGetLastError());
+      hipLaunchKernelGGL(km_queue_join_kernel, dim3(a.bh), dim3(kThreads), 0, s, tflags, tcount,
+                         a.n, tph, flags, ctl);
       SVA_CHECK(hipGetLastError());
       hipLaunchKernelGGL((km_assign_mfma_kernel<D, true>), tok_grid, dim3(kThreads), 0, s,
                          static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, ctl,
-                         a.centroids, a.assign, flags, ctl, a.n_refined, a.bh, tph);
+                         a.centroids, a.assign, flags, tflags, tcount, a.n_refined, a.bh, tph);
       SVA_CHECK(hipGetLastError());
     } else {
       hipLaunchKernelGGL((km_assign_f64_kernel<D>), dim3((a.n + kThreads - 1) / kThreads, a.bh),
@@ -514,7 +664,7 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
                          a.centroids, a.assign);
       SVA_CHECK(hipGetLastError());
     }
-    // the sort's scan clears both per-slice counters for the next iteration
+    // the sort's scan clears the per-slice queue lengths for the next iteration
     SVA_CHECK(launch_cluster_sort(a.assign, a.bh, a.n, a.c, perm, offsets,
                                   last ? a.sizes : nullptr, sort_ws, s, bf16 ? ctl : nullptr));
     SVA_CHECK(mean((bf16 && !last) ? 1 : 2));

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(kThreads) void sort_hist_rank_kernel(
   for (int base = t0; base < t1; base += kThreads) {
     const int i = base + tid;
     const bool valid = i < t1;
-    const int key = valid ? a[i] : 0;
+    // ids outside [0, c) are clamped, so no input can index outside the tables
+    const int key = valid ? min(max(a[i], 0), c - 1) : 0;
     uint64_t eq = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (key >> b) & 1;
@@ -89,10 +90,7 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(
   }
   if (tid == 0) {
     off[c] = n;
-    if (clear != nullptr) {            // per-slice counters of the caller, [2][slices]
-      clear[bh] = 0;
-      clear[gridDim.x + bh] = 0;
-    }
+    if (clear != nullptr) clear[bh] = 0;   // a per-slice counter of the caller
   }
   if (sizes != nullptr) {
     int32_t *sz = sizes + static_cast<size_t>(bh) * c;
@@ -111,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
   const size_t row = static_cast<size_t>(bh) * n + i;
-  const int key = assign[row];
+  const int key = min(max(assign[row], 0), c - 1);   // as in hist_rank
   const int pos = base[(static_cast<size_t>(bh) * c + key) * tiles + i / kTile] + rank[row];
   perm[static_cast<size_t>(bh) * n + pos] = i;
 }

@@ -75,7 +75,7 @@ size_t kmeans_ws_bytes(int32_t bh, int32_t n, int32_t d, int32_t c);
 hipError_t launch_kmeans(const KmeansArgs &a, hipStream_t s);
 
 // stable counting sort of rows by cluster id (shared by k-means and permute);
-// `clear`, if not NULL, holds 2*bh ints that the sort sets to zero
+// `clear`, if not NULL, holds bh ints that the sort sets to zero
 size_t sort_ws_bytes(int32_t bh, int32_t n, int32_t c);
 hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int32_t c,
                                int32_t *perm, int32_t *offsets, int32_t *sizes, void *ws,
