@@ -4,8 +4,9 @@ Workload (default): the 5 s clip layer -- 32,760 latent tokens (21x30x52 grid)
 x 40 heads, d=128, bf16; k-means with C_q=100 / C_k=500 for 10 iterations,
 top-p 0.9; seeded synthetic mixture-of-Gaussians tokens (centre scale 1.75,
 about 85% sparsity).  A step is one pass of the whole hot path: k-means of Q
-and of K, permutation of Q and of K/V, top-p selection, block-sparse
-attention, unpermutation.  Inputs are resident in HBM before timing.
+and of K, permutation of Q and of K/V (the Q side on a second stream,
+concurrently with the K/V side), top-p selection, block-sparse attention,
+unpermutation.  Inputs are resident in HBM before timing.
 
 Prints one JSON line: value = effective TFLOP/s of the layer (4 d x kept
 (query, key) pairs per step / step time), ms_per_step = ms per layer, plus the
@@ -118,26 +119,24 @@ def main() -> int:
     del x
     layer = SparseVideoAttention(cfg.batch, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
                                  cfg.top_p, device=dev)
-    stages = ("kmeans", "permute", "select", "attention", "unpermute")
+    # "cluster" = k-means + permutation of Q (side stream) and of K/V, joined
+    stages = ("cluster", "select", "attention", "unpermute")
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        layer.kmeans(t["q"], t["k"], iq, ik)
+        layer.cluster(t["q"], t["k"], t["v"], iq, ik)
         if ev is not None:
             ev[1].record()
-        layer.permute(t["q"], t["k"], t["v"])
-        if ev is not None:
-            ev[2].record()
         layer.select()
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
         layer.attend()
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
         layer.unpermute()
         if ev is not None:
-            ev[5].record()
+            ev[4].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -148,7 +147,8 @@ def main() -> int:
     flops = 4.0 * cfg.d * kept
 
     log(f"[bench] timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -159,7 +159,8 @@ def main() -> int:
     per_stage = {name: statistics.median(events[s][i].elapsed_time(events[s][i + 1])
                                          for s in range(args.steps))
                  for i, name in enumerate(stages)}
-    attn_ms = statistics.mean(events[s][3].elapsed_time(events[s][4]) for s in range(args.steps))
+    ia = stages.index("attention")
+    attn_ms = statistics.mean(events[s][ia].elapsed_time(events[s][ia + 1]) for s in range(args.steps))
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
 
     dense = None

@@ -39,6 +39,7 @@
 
 #include "../../include/sva.h"
 #include "sva_internal.h"
+#include "lds_pipe.h"
 
 namespace sva {
 namespace {
@@ -75,108 +76,6 @@ __host__ __device__ constexpr int vswz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-// Wait until at most N vector-memory loads of this wave are outstanding (loads
-// complete in issue order).  N < 16; expcnt and lgkmcnt are left unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// Byte offset of a __shared__ object in the workgroup's LDS (the address the
-// ds_* instructions take).
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
-}
-
-// MFMA operand fragments read from LDS in inline assembly.  The K/V stages are
-// filled by global->LDS copies that stay in flight across the reads of other
-// stages; reads the compiler can see would make it wait for every such copy
-// first (vmcnt(0)), so these reads are kept out of its sight, and the explicit
-// vmcnt wait plus barrier at the top of each step orders them instead.  Each
-// block waits for its own reads before returning (lgkmcnt(0)).
-//
-// K: n = 4 or 8 ds_read_b128, lane address a[s] + OFF.
-template <int OFF, int N>
-__device__ __forceinline__ void lds_read_frags(bf16x8 (&f)[N], const uint32_t (&a)[N]) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-  if constexpr (N == 8) {
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:%16\n\t"
-        "ds_read_b128 %1, %9 offset:%16\n\t"
-        "ds_read_b128 %2, %10 offset:%16\n\t"
-        "ds_read_b128 %3, %11 offset:%16\n\t"
-        "ds_read_b128 %4, %12 offset:%16\n\t"
-        "ds_read_b128 %5, %13 offset:%16\n\t"
-        "ds_read_b128 %6, %14 offset:%16\n\t"
-        "ds_read_b128 %7, %15 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
-          "=&v"(f[6]), "=&v"(f[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-          "v"(a[7]), "i"(OFF)
-        : "memory");
-  } else {
-    static_assert(N == 4, "4 or 8 fragments");
-    asm volatile(
-        "ds_read_b128 %0, %4 offset:%8\n\t"
-        "ds_read_b128 %1, %5 offset:%8\n\t"
-        "ds_read_b128 %2, %6 offset:%8\n\t"
-        "ds_read_b128 %3, %7 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
-        : "memory");
-  }
-}
-
-// V^T: for each of N d tiles two ds_read_b64_tr_b16 (rows +0 and +HI of the
-// k-step) joined into one 8-element operand.
-template <int OFF, int HI, int N>
-__device__ __forceinline__ void lds_read_vt(bf16x8 (&f)[N], const uint32_t (&a)[N]) {
-  static_assert(OFF >= 0 && OFF + HI < 65536, "ds offset field");
-  bf16x4 lo[N], hi[N];
-  if constexpr (N == 4) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
-          "=&v"(lo[3]), "=&v"(hi[3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + HI)
-        : "memory");
-  } else {
-    static_assert(N == 2, "2 or 4 d tiles");
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
-        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
-        : "v"(a[0]), "v"(a[1]), "i"(OFF), "i"(OFF + HI)
-        : "memory");
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) f[i] = __builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Workgroup barrier for LDS only: this wave's LDS accesses complete, then
-// s_barrier.  Unlike __syncthreads() it does not wait for outstanding
-// global->LDS copies, which the K/V pipeline keeps in flight across it; the
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // In-place exclusive scan of a[0..n) (n <= 4*NTHREADS) held in LDS; writes
 // the total to a[n].  Must be called by all NTHREADS threads of the workgroup.

@@ -31,10 +31,14 @@
 //   results are deterministic; an empty cluster keeps its centroid.  The same kernel splits the new centroids
 //   into hi/lo bf16 and computes -||c||^2/2 for the next assign (whose
 //   workgroups take max ||c|| of their slice from it).
+#include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "../../include/sva.h"
 #include "sva_internal.h"
+#include "lds_pipe.h"
 
 namespace sva {
 namespace {
@@ -78,32 +82,29 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA assignment (REFINE = false) and fp64 refinement of queued rows (true)
+// MFMA assignment, main pass.  A workgroup holds kTokTile tokens of one slice
+// in registers (MFMA B operands) and streams the slice's centroid tiles (32
+// clusters, hi and lo split, plus their -||c||^2/2) through a three-stage LDS
+// ring filled by direct global->LDS copies two tiles ahead; one partial vmcnt
+// wait and one barrier per tile.
 // ---------------------------------------------------------------------------
-template <int D, bool REFINE>
-__global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
     const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
     const uint16_t *__restrict__ clo, const float *__restrict__ nh,
-    const int32_t *__restrict__ ctl, const float *__restrict__ cent,
-    int32_t *__restrict__ assign, int2 *__restrict__ flags, int2 *__restrict__ tflags,
-    int32_t *__restrict__ tcount, int32_t *__restrict__ n_refined, int nbh, int tph) {
+    int32_t *__restrict__ assign, int2 *__restrict__ tflags, int32_t *__restrict__ tcount,
+    int nbh, int tph) {
   constexpr int NS = D / 16;
-  constexpr int KCH = D / 8;                 // 16-byte chunks per centroid row
-  constexpr int CPT = KCH / 4;               // chunks per thread per tile load
-  constexpr int CC = REFINE ? kCandCap : 1;
-  // the refine pass takes 32 queued rows per wave: more workgroups share a queue
-  constexpr int NT = REFINE ? 1 : kNT;
-  constexpr int TOKT = NT * 32 * (kThreads / 64);
-  constexpr int TS = REFINE ? TOKT : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t sC[2][2][32 * D];
-  __shared__ __attribute__((aligned(16))) float sN[2][32];
-  __shared__ int32_t s_cand[CC];
-  __shared__ double s_dist[CC];
-  __shared__ unsigned long long s_bestd[TS];
-  __shared__ int32_t s_bestc[TS];
-  __shared__ int32_t s_tok[TS];
-  __shared__ int32_t s_over[TS];
-  __shared__ int32_t s_ncand;
+  constexpr int NT = kNT;
+  constexpr int PPR = D / 8;                          // 16-byte pieces per centroid row
+  constexpr int RPI = 64 / PPR;                       // rows per 1 KB wave copy
+  constexpr int BPS = 32 / RPI;                       // wave copies per split per tile
+  constexpr int CPW = 2 * BPS / (kThreads / 64);      // wave copies per wave per tile
+  static_assert(CPW >= 1 && CPW < 15, "copy split");
+  constexpr int kSplitB = 32 * D * 2;                 // bytes of one split of a tile
+  constexpr int kStageB = 2 * kSplitB;
+  __shared__ __attribute__((aligned(16))) uint16_t sC[3][2][32 * D];
+  __shared__ __attribute__((aligned(16))) float sN[3][64];   // [32, 64): copy padding
   __shared__ int32_t s_wq[kThreads / 64];
   __shared__ float s_nhmin[kThreads / 64];
 
@@ -118,7 +119,256 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
   const int h = lane >> 5, col = lane & 31;
   const int ntl = cpad / 32;
   const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
-  const int ntok = REFINE ? ctl[bh] : n;
+  const size_t cbase = static_cast<size_t>(bh) * cpad;
+
+  // copy geometry: wave copy j of a tile fills LDS bytes [1 KB * blk, +1 KB) of
+  // split blk / BPS (blk = wave * CPW + j); lane l fills physical piece l % PPR
+  // of row RPI * (blk % BPS) + l / PPR, i.e. the row's logical piece
+  // (l % PPR) ^ swizzle(row).  Each wave also copies the tile's 32 -||c||^2/2.
+  const int cp_rsub = lane / PPR, cp_piece = lane % PPR;
+  auto issue_tile = [&](int ct, auto st) {
+    constexpr int S = decltype(st)::value;
+    const int t = ct < ntl ? ct : 0;                  // past the end: reload tile 0
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int blk = wave * CPW + j;
+      const int sp = blk / BPS, rb = blk % BPS;
+      const int r = rb * RPI + cp_rsub;
+      const size_t goff = (cbase + t * 32 + r) * D + ((cp_piece ^ cswz<D>(r)) << 3);
+      const uint16_t *src = (sp ? clo : chi) + goff;
+      uint16_t *dst = &sC[S][sp][rb * RPI * D];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+    {   // every wave copies the same 32 values (no branch, uniform copy counts);
+        // lanes 32-63 repeat them into the padding
+      const float *src = nh + cbase + t * 32 + (lane & 31);
+      float *dst = &sN[S][0];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+    }
+  };
+
+  // ring prologue first: the compiler's wait for the token registers below
+  // covers every load in flight (it cannot order plain loads against
+  // global->LDS copies), so the copies are issued before anything it waits for
+  issue_tile(0, std::integral_constant<int, 0>{});
+  issue_tile(1, std::integral_constant<int, 1>{});
+  asm volatile("" ::: "memory");
+
+  // this workgroup's tokens: B operands of 32x32x16 MFMAs, lane holds
+  // x[token][16 s + 8 h .. +8] of its token column
+  int tok[NT];
+  bool tv[NT];
+  bf16x8 xf[NT][NS];
+  const int base = tile * kTokTile;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    tok[nt] = base + wave * (NT * 32) + nt * 32 + col;
+    tv[nt] = tok[nt] < n;
+    // columns past the end load row n-1 unconditionally (a conditional load
+    // makes the compiler wait for it at the branch join); their results are
+    // never used
+    const uint16_t *row = xb + static_cast<size_t>(tv[nt] ? tok[nt] : n - 1) * D + h * 8;
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)
+      xf[nt][s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + s2 * 16));
+  }
+  // -||c||^2/2 of the slice's real clusters, for max ||c||
+  float mn = 0.f;
+  for (int j0 = 0; j0 < c; j0 += 4 * kThreads) {
+    float v4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = j0 + k * kThreads + tid;
+      v4[k] = j < c ? nh[cbase + j] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mn = fminf(mn, v4[k]);
+  }
+
+  // per-wave minimum of -||c||^2/2, read after the barriers below
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
+  if (lane == 0) s_nhmin[wave] = mn;
+
+  // ||x|| bound per token
+  float nx[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float p = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = static_cast<float>(xf[nt][s2][j]);
+        p = fmaf(f, f, p);
+      }
+    p += __shfl_xor(p, 32);
+    nx[nt] = sqrtf(p) * (1.f + 0x1p-10f);
+  }
+
+  // LDS byte addresses of this lane's A fragments (centroid row col, piece
+  // 2s+h) and -||c||^2/2 values in stage 0, split 0
+  uint32_t ka[NS];
+  const uint32_t sc0 = lds_offset(&sC[0][0][0]);
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) ka[s2] = sc0 + col * D * 2 + (((2 * s2 + h) ^ cswz<D>(col)) << 4);
+  const uint32_t na = lds_offset(&sN[0][0]) + 16 * h;
+
+  // best and second-best w of the lane's clusters; the best's row within its
+  // tile rides in the 4 low mantissa bits of the tracked values, its tile in t1
+  float b1[NT], b2[NT];
+  int t1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    b1[nt] = -INFINITY;
+    b2[nt] = -INFINITY;
+    t1[nt] = 0;
+  }
+
+  auto step = [&](auto st, int ct) {
+    constexpr int S = decltype(st)::value;
+    // tile ct has landed once only tile ct+1's copies are outstanding; after
+    // the barrier every wave's copies of tile ct are in LDS and every wave is
+    // done with tile ct-1, whose stage tile ct+2 then refills
+    wait_vmcnt<CPW + 1>();
+    lds_barrier();
+    issue_tile(ct + 2, std::integral_constant<int, (S + 2) % 3>{});
+    f32x4 n4[4];                                      // -||c||^2/2 of the lane's 16 rows
+    lds_read_f32x4x4<S * 256, 32>(n4, na);
+    f32x16 cinit;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cinit[4 * g + j] = n4[g][j];
+    f32x16 acc[NT];
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      bf16x8 af[NS];
+      if (sp == 0) lds_read_frags<S * kStageB>(af, ka);
+      else lds_read_frags<S * kStageB + kSplitB>(af, ka);
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = mfma32x32x16(af[s2], xf[nt][s2], (sp == 0 && s2 == 0) ? cinit : acc[nt]);
+    }
+    // w with its accumulator index i (0..15) in the 4 low mantissa bits: one
+    // and-or, and max / med3 then carry the index along (the change of w,
+    // below 2^-19 |w|, is part of the error bound)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float prev = b1[nt];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float we = __int_as_float((__float_as_int(acc[nt][i]) & ~15) | i);
+        b2[nt] = __builtin_amdgcn_fmed3f(b1[nt], b2[nt], we);
+        b1[nt] = __builtin_elementwise_maximum(b1[nt], we);
+      }
+      t1[nt] = b1[nt] != prev ? ct : t1[nt];
+    }
+  };
+  for (int ct = 0; ct < ntl; ct += 3) {
+    step(std::integral_constant<int, 0>{}, ct);
+    if (ct + 1 < ntl) step(std::integral_constant<int, 1>{}, ct + 1);
+    if (ct + 2 < ntl) step(std::integral_constant<int, 2>{}, ct + 2);
+  }
+  wait_vmcnt<0>();   // the copies past the end land before the workgroup ends
+
+  // error bound E of every w of a token (split residual of the centroid, fp32
+  // accumulation of 2d exact products and the start value, final rounding,
+  // index bits), from ||x|| and the slice's max ||c|| (with margin)
+  float nhmin = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) nhmin = fminf(nhmin, s_nhmin[w]);
+  const float cm = sqrtf(-2.f * nhmin) * (1.f + 0x1p-20f);
+  // decided rows are assigned; the others are compacted, in wave and lane
+  // order, into this tile's region of the slice's queue area (tflags), with
+  // their count in tcount; a join kernel then concatenates the regions
+  bool queued[NT];
+  uint64_t qm[NT];
+  int thr_bits[NT];
+  int wq = 0;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx[nt] * cm +
+                    (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx[nt] * cm) +
+                    0x1p-19f * (nx[nt] * cm + 0.5f * cm * cm);
+    const float two_e = 2.f * 1.25f * e;
+    const int i1 = t1[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
+    const float ob1 = __shfl_xor(b1[nt], 32), ob2 = __shfl_xor(b2[nt], 32);
+    const int oi1 = __shfl_xor(i1, 32);
+    const bool other = ob1 > b1[nt] || (ob1 == b1[nt] && oi1 < i1);
+    const float nb1 = fmaxf(b1[nt], ob1);
+    const int ival = other ? oi1 : i1;
+    const float nb2 = fmaxf(fminf(b1[nt], ob1), fmaxf(b2[nt], ob2));
+    const bool decided = nb1 - nb2 > two_e;
+    if (h == 0 && tv[nt] && decided) assign[static_cast<size_t>(bh) * n + tok[nt]] = ival;
+    queued[nt] = h == 0 && tv[nt] && !decided;
+    thr_bits[nt] = __float_as_int(nb1 - two_e);
+    qm[nt] = __ballot(queued[nt]);
+    wq += __popcll(qm[nt]);
+  }
+  if (lane == 0) s_wq[wave] = wq;
+  __syncthreads();
+  int q = base, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    q += w < wave ? s_wq[w] : 0;
+    tot += s_wq[w];
+  }
+  const uint64_t lt = (1ull << lane) - 1;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (queued[nt])
+      tflags[static_cast<size_t>(bh) * n + q + __popcll(qm[nt] & lt)] = int2{tok[nt], thr_bits[nt]};
+    q += __popcll(qm[nt]);
+  }
+  if (tid == 0) tcount[static_cast<size_t>(bh) * tph + tile] = tot;
+}
+// ---------------------------------------------------------------------------
+// fp64 refinement of the queued rows: the queued rows run through the same
+// MFMA loop (centroid tiles staged through registers into two LDS buffers);
+// every cluster with w >= the row's threshold goes to an LDS candidate list,
+// one lane per candidate computes the exact fp64 distance, and the smallest
+// distance wins, ties to the lowest index.  Grid-stride over the slice's
+// queue, 32 rows per wave.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void km_refine_kernel(
+    const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
+    const uint16_t *__restrict__ clo, const float *__restrict__ nh,
+    const int32_t *__restrict__ qcount, const float *__restrict__ cent,
+    int32_t *__restrict__ assign, const int2 *__restrict__ flags,
+    int32_t *__restrict__ n_refined, int nbh, int tph) {
+  constexpr int NS = D / 16;
+  constexpr int KCH = D / 8;                 // 16-byte chunks per centroid row
+  constexpr int CPT = KCH / 4;               // chunks per thread per tile load
+  constexpr int CC = kCandCap;
+  constexpr int NT = 1;                      // 32 queued rows per wave
+  constexpr int TOKT = NT * 32 * (kThreads / 64);
+  constexpr int TS = TOKT;
+  __shared__ __attribute__((aligned(16))) uint16_t sC[2][2][32 * D];
+  __shared__ __attribute__((aligned(16))) float sN[2][32];
+  __shared__ int32_t s_cand[CC];
+  __shared__ double s_dist[CC];
+  __shared__ unsigned long long s_bestd[TS];
+  __shared__ int32_t s_bestc[TS];
+  __shared__ int32_t s_tok[TS];
+  __shared__ int32_t s_over[TS];
+  __shared__ int32_t s_ncand;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; slices are dealt
+  // to XCDs the same way, so all tiles of a slice run on one XCD and its
+  // centroids stay in that XCD's L2.  tph = token tiles per slice.
+  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (k8 / tph);
+  const int tile = k8 % tph;
+  if (bh >= nbh) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int ntl = cpad / 32;
+  const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
+  const int ntok = qcount[bh];
   const int step = tph * TOKT;
 
   // tile loader: thread -> (split, row, quarter of the row)
@@ -143,8 +393,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
     if (tid < 32) sN[buf][tid] = nreg;
   };
 
-  // main pass: one tile of tokens per workgroup; refine: grid-stride over the queue
-  for (int base = tile * TOKT; base < ntok; base = REFINE ? base + step : ntok) {
+  for (int base = tile * TOKT; base < ntok; base += step) {
     int tok[NT];
     bool tv[NT];
     float thr[NT];
@@ -156,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
       tv[nt] = idx < ntok;
       tok[nt] = idx;
       thr[nt] = 0.f;
-      if (REFINE && tv[nt]) {
+      if (tv[nt]) {
         const int2 e = flags[static_cast<size_t>(bh) * n + idx];
         tok[nt] = e.x;
         thr[nt] = __int_as_float(e.y);
@@ -167,51 +416,14 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
         const u32x4 raw = tv[nt] ? *reinterpret_cast<const u32x4 *>(row + s * 16) : u32x4{0, 0, 0, 0};
         xf[nt][s] = __builtin_bit_cast(bf16x8, raw);
       }
-      if constexpr (REFINE) {
-        if (h == 0) {
-          s_tok[slot] = tv[nt] ? tok[nt] : -1;
-          s_over[slot] = 0;
-          s_bestd[slot] = ~0ull;
-          s_bestc[slot] = 0x7fffffff;
-        }
+      if (h == 0) {
+        s_tok[slot] = tv[nt] ? tok[nt] : -1;
+        s_over[slot] = 0;
+        s_bestd[slot] = ~0ull;
+        s_bestc[slot] = 0x7fffffff;
       }
     }
-    if constexpr (REFINE) {
-      if (tid == 0) s_ncand = 0;
-    }
-    // ||x|| bound per token (main pass), for the error bound of w
-    float nx[NT];
-    if constexpr (!REFINE) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float p = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float f = static_cast<float>(xf[nt][s][j]);
-            p = fmaf(f, f, p);
-          }
-        p += __shfl_xor(p, 32);
-        nx[nt] = sqrtf(p) * (1.f + 0x1p-10f);
-      }
-      // max ||c|| of the slice from -||c||^2/2 of its real clusters (the
-      // per-wave minima are read after the first barrier below)
-      float mn = 0.f;
-      for (int j = tid; j < c; j += kThreads) mn = fminf(mn, nh[static_cast<size_t>(bh) * cpad + j]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
-      if (lane == 0) s_nhmin[wave] = mn;
-    }
-
-    float b1[NT], b2[NT];
-    int i1[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      b1[nt] = -INFINITY;
-      b2[nt] = -INFINITY;
-      i1[nt] = 0;
-    }
+    if (tid == 0) s_ncand = 0;
 
     load_tile(0);
     store_tile(0);
@@ -243,78 +455,18 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_mfma_kernel(
         for (int i = 0; i < 16; ++i) {
           const int cl = ct * 32 + acc_row(i, h);
           const float w = acc[nt][i];
-          if constexpr (!REFINE) {
-            const bool gt = w > b1[nt];
-            b2[nt] = __builtin_amdgcn_fmed3f(b1[nt], b2[nt], w);
-            b1[nt] = fmaxf(b1[nt], w);
-            i1[nt] = gt ? cl : i1[nt];
-          } else {
-            if (tv[nt] && cl < c && w >= thr[nt]) {
-              const int slot = wave * (NT * 32) + nt * 32 + col;
-              const int k = atomicAdd(&s_ncand, 1);
-              if (k < kCandCap) s_cand[k] = (slot << 14) | cl;
-              else s_over[slot] = 1;
-            }
+          if (tv[nt] && cl < c && w >= thr[nt]) {
+            const int slot = wave * (NT * 32) + nt * 32 + col;
+            const int k = atomicAdd(&s_ncand, 1);
+            if (k < kCandCap) s_cand[k] = (slot << 14) | cl;
+            else s_over[slot] = 1;
           }
         }
       if (ct + 1 < ntl) store_tile(buf ^ 1);
       __syncthreads();
     }
 
-    if constexpr (!REFINE) {
-      // error bound E of every w of a token (split residual of the centroid,
-      // fp32 accumulation of 2d exact products and the start value, final
-      // rounding), from ||x|| and the slice's max ||c|| (with margin)
-      float nhmin = 0.f;
-#pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) nhmin = fminf(nhmin, s_nhmin[w]);
-      const float cm = sqrtf(-2.f * nhmin) * (1.f + 0x1p-20f);
-      float two_e[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx[nt] * cm +
-                        (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx[nt] * cm);
-        two_e[nt] = 2.f * 1.25f * e;
-      }
-      // decided rows are assigned; the others are compacted, in wave and lane
-      // order, into this tile's region of the slice's queue area (tflags), with
-      // their count in tcount; a compaction kernel then joins the regions
-      bool queued[NT];
-      uint64_t qm[NT];
-      int ival[NT], thr_bits[NT];
-      int wq = 0;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float ob1 = __shfl_xor(b1[nt], 32), ob2 = __shfl_xor(b2[nt], 32);
-        const int oi1 = __shfl_xor(i1[nt], 32);
-        const bool other = ob1 > b1[nt] || (ob1 == b1[nt] && oi1 < i1[nt]);
-        const float nb1 = fmaxf(b1[nt], ob1);
-        ival[nt] = other ? oi1 : i1[nt];
-        const float nb2 = fmaxf(fminf(b1[nt], ob1), fmaxf(b2[nt], ob2));
-        const bool decided = nb1 - nb2 > two_e[nt];
-        if (h == 0 && tv[nt] && decided) assign[static_cast<size_t>(bh) * n + tok[nt]] = ival[nt];
-        queued[nt] = h == 0 && tv[nt] && !decided;
-        thr_bits[nt] = __float_as_int(nb1 - two_e[nt]);
-        qm[nt] = __ballot(queued[nt]);
-        wq += __popcll(qm[nt]);
-      }
-      if (lane == 0) s_wq[wave] = wq;
-      __syncthreads();
-      int q = tile * TOKT, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) {
-        q += w < wave ? s_wq[w] : 0;
-        tot += s_wq[w];
-      }
-      const uint64_t lt = (1ull << lane) - 1;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (queued[nt])
-          tflags[static_cast<size_t>(bh) * n + q + __popcll(qm[nt] & lt)] = int2{tok[nt], thr_bits[nt]};
-        q += __popcll(qm[nt]);
-      }
-      if (tid == 0) tcount[static_cast<size_t>(bh) * tph + tile] = tot;
-    } else {
+    {
       // exact fp64 distance of every candidate, one lane per candidate (rows read
       // as 16-byte pieces, summed in ascending dimension order)
       const int ncand = min(s_ncand, kCandCap);
@@ -591,8 +743,10 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+  // padding rows of the last tile start their w at -FLT_MAX: finite, so the
+  // index bits the assign pass writes into w's mantissa never make a NaN
   if (lane == 0)
-    nh[static_cast<size_t>(bh) * cpad + cl] = real ? static_cast<float>(-0.5 * sq) : -INFINITY;
+    nh[static_cast<size_t>(bh) * cpad + cl] = real ? static_cast<float>(-0.5 * sq) : -FLT_MAX;
 }
 
 template <int D>
@@ -647,16 +801,16 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   for (int it = 0; it < a.iters; ++it) {
     const bool last = it + 1 == a.iters;
     if (bf16) {
-      hipLaunchKernelGGL((km_assign_mfma_kernel<D, false>), tok_grid, dim3(kThreads), 0, s,
-                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, ctl,
-                         a.centroids, a.assign, flags, tflags, tcount, a.n_refined, a.bh, tph);
+      hipLaunchKernelGGL((km_assign_main_kernel<D>), tok_grid, dim3(kThreads), 0, s,
+                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
+                         a.assign, tflags, tcount, a.bh, tph);
       SVA_CHECK(hipGetLastError());
       hipLaunchKernelGGL(km_queue_join_kernel, dim3(a.bh), dim3(kThreads), 0, s, tflags, tcount,
                          a.n, tph, flags, ctl);
       SVA_CHECK(hipGetLastError());
-      hipLaunchKernelGGL((km_assign_mfma_kernel<D, true>), tok_grid, dim3(kThreads), 0, s,
+      hipLaunchKernelGGL((km_refine_kernel<D>), tok_grid, dim3(kThreads), 0, s,
                          static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, ctl,
-                         a.centroids, a.assign, flags, tflags, tcount, a.n_refined, a.bh, tph);
+                         a.centroids, a.assign, flags, a.n_refined, a.bh, tph);
       SVA_CHECK(hipGetLastError());
     } else {
       hipLaunchKernelGGL((km_assign_f64_kernel<D>), dim3((a.n + kThreads - 1) / kThreads, a.bh),

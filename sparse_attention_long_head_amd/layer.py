@@ -5,8 +5,12 @@ Sparse VideoGen2 explainer, technical summary section 2: k-means of Q and K
 (2.b), attention over the kept blocks (2.c), inverse permutation (2.a).
 
 ``SparseVideoAttention`` owns every buffer the layer needs (allocated once,
-through torch), so ``forward`` only enqueues the seven library calls on the
-current stream: it allocates nothing and never synchronises.
+through torch), so ``forward`` only enqueues the library calls: it allocates
+nothing and never synchronises.  The clustering and permutation of Q run on a
+side stream concurrently with those of K and V on the current stream (the two
+are independent until the selection); the current stream waits for the side
+stream before the selection, so to a caller the layer is ordered on the
+current stream like any other op.
 """
 from __future__ import annotations
 
@@ -58,6 +62,9 @@ class SparseVideoAttention:
                  lib.sva_permute_workspace_bytes(batch, heads, n, ck))
         at = lib.sva_attn_workspace_bytes(batch, heads, n, cq)
         self.ws = torch.empty(max(km, pm, at, 1), dtype=torch.uint8, device=dev)
+        # the Q clustering runs on a side stream with a workspace of its own
+        self.ws_q = torch.empty(max(km, pm, 1), dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
 
     # the individual stages, so callers (and the benchmark) can time them
     def kmeans(self, q, k, init_q, init_k):
@@ -83,9 +90,26 @@ class SparseVideoAttention:
     def unpermute(self):
         L.sva_unpermute(self.o_p, self.perm_q, self.o)
 
+    def cluster(self, q, k, v, init_q, init_k):
+        """k-means and permutation of Q (side stream) and of K, V (current
+        stream), concurrently; returns with the current stream ordered after
+        both."""
+        cur = torch.cuda.current_stream(self.ws.device)
+        self.side.wait_stream(cur)
+        with torch.cuda.stream(self.side):
+            self.cent_q.copy_(init_q)
+            L.sva_kmeans(q, self.cq, self.iters, self.cent_q, self.assign_q, self.sizes_q,
+                         ws=self.ws_q)
+            L.sva_permute(self.assign_q, self.cq, [q], self.perm_q, self.off_q, [self.q_p],
+                          ws=self.ws_q)
+        self.cent_k.copy_(init_k)
+        L.sva_kmeans(k, self.ck, self.iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
+        L.sva_permute(self.assign_k, self.ck, [k, v], self.perm_k, self.off_k,
+                      [self.k_p, self.v_p], ws=self.ws)
+        cur.wait_stream(self.side)
+
     def forward(self, q, k, v, init_q, init_k) -> torch.Tensor:
-        self.kmeans(q, k, init_q, init_k)
-        self.permute(q, k, v)
+        self.cluster(q, k, v, init_q, init_k)
         self.select()
         self.attend()
         self.unpermute()

@@ -132,3 +132,27 @@ def test_full_size_output_sampled(full_layer):
                                                 aq[0, h], ak[0, h], mask[0, h],
                                                 np.float32(layer.scale), rows=rows)
         check_attention(o[0, h, rows], ro, True, f"layer head {h}")
+
+
+def test_two_stream_forward_equals_sequential_stages():
+    # forward runs the Q clustering on a side stream, concurrently with K/V;
+    # the result must be bit-identical to the stages run one after another
+    cfg = synth.CONFIGS["5s"].with_(heads=4)
+    x, iq, ik = _layer_inputs(cfg, heads=(0, 1, 2, 3))
+    dev = device()
+    layer = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
+                                 cfg.top_p, device=dev)
+    t = {k: to_dev(v, torch.bfloat16) for k, v in x.items()}
+    iq_d, ik_d = to_dev(iq), to_dev(ik)
+    outs = []
+    for _ in range(2):
+        layer(t["q"], t["k"], t["v"], iq_d, ik_d)
+        outs.append(layer.o.clone())
+    layer.kmeans(t["q"], t["k"], iq_d, ik_d)
+    layer.permute(t["q"], t["k"], t["v"])
+    layer.select()
+    layer.attend()
+    layer.unpermute()
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], layer.o)
