@@ -53,8 +53,9 @@ def attention_traffic():
         return None
 
 
-def cpu_baseline(cfg, heads=(0, 1, 2)):
-    """The fp64 oracle's whole layer on a few heads (same tensors, same seeds)."""
+def cpu_baseline(cfg, heads=(0, 1, 2, 3, 4, 5)):
+    """The fp64 oracle's whole layer on a few heads (same tensors, same seeds); about
+    10-20 s of host time at the 5 s clip size."""
     import oracle
     import synth
     try:
