@@ -35,6 +35,7 @@
 // small correctness workloads).
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "../../include/sva.h"
@@ -55,8 +56,34 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 struct WorkItem {
-  int32_t qb, row0;
+  int32_t bh, qb, row0, cost;   // cost: 64-key chunks of the item + kItemFixed
 };
+constexpr int kItemFixed = 3;          // per-item setup/epilogue cost, in chunk units
+constexpr int kOrderThreads = 1024;    // the single workgroup that orders the work
+constexpr int kOrderBuckets = 1024;    // cost buckets of the ordering sort
+constexpr int kMaxOrderHeads = 4096;   // slices balanced over XCDs (more: slice % 8)
+
+// Schedule scratch inside the attention workspace
+struct SchedLayout {
+  size_t items, qcost, hinfo, lists, ctl, total;
+};
+inline SchedLayout sched_layout(int32_t bh, int32_t n_q, int32_t nqb) {
+  const size_t cap = static_cast<size_t>((n_q + kQTile - 1) / kQTile) + nqb;
+  SchedLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes, 256);
+    return at;
+  };
+  L.items = take(static_cast<size_t>(bh) * cap * sizeof(WorkItem));   // [bh][cap], per slice
+  L.qcost = take(static_cast<size_t>(bh) * nqb * 4);                  // [bh][nqb] chunk cost
+  L.hinfo = take(static_cast<size_t>(bh) * 2 * 4);                    // [bh] cost sum, items
+  L.lists = take(static_cast<size_t>(bh) * cap * sizeof(WorkItem));   // per-XCD ordered lists
+  L.ctl = take(32 * 4);                                               // count[8] start[8] ctr[8]
+  L.total = off;
+  return L;
+}
 
 // XOR swizzle of the 16-byte pieces of K row r (rows of 256 B for d=128,
 // 128 B for d=64): the ds_read_b128 of an S^T operand has 16 lanes on 16
@@ -127,41 +154,187 @@ __device__ __forceinline__ bool decode_work(const WorkItem *work, int work_cap, 
   return qb >= 0;
 }
 
+// Next item of a persistent workgroup (thread 0 only): the queue of the
+// workgroup's XCD first, then the others (work stealing); -1 when all are
+// drained.  `gone` remembers queues this workgroup found empty.
+__device__ __forceinline__ int fetch_work(int32_t *ctl, int &gone) {
+  const int x0 = blockIdx.x & 7;
+  for (int k = 0; k < 8; ++k) {
+    const int y = (x0 + k) & 7;
+    if (gone & (1 << y)) continue;
+    const int i = atomicAdd(&ctl[16 + y], 1);
+    if (i < ctl[y]) return ctl[8 + y] + i;
+    gone |= 1 << y;
+  }
+  return -1;
+}
+
 // ---------------------------------------------------------------------------
-// schedule: one work item per 128-row tile of every Q block
+// schedule, sparse mode
+//   cost:  one wave per Q block adds up its kept clusters' sizes L; the cost of
+//          each 256-row tile of the block is ceil(L / 64) chunks + kItemFixed
+//   items: per slice, one item per tile, in block order (the fp32 kernel walks
+//          these directly); plus the slice's cost sum and item count
+//   order: one workgroup deals slices to the 8 XCDs (largest first, each to
+//          the least loaded) and sorts each XCD's items by descending cost;
+//          the bf16 kernel's persistent workgroups take them from these queues
+//          (longest processing time first) and steal from other XCDs' queues
+//          when their own is empty
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void attn_schedule_kernel(const int32_t *__restrict__ q_off,
-                                                                 int nqb, int work_cap,
-                                                                 WorkItem *__restrict__ work) {
+__global__ __launch_bounds__(kThreads) void attn_cost_kernel(
+    const int32_t *__restrict__ k_off, const int32_t *__restrict__ kept_count,
+    const int32_t *__restrict__ kept_idx, int kept_stride, int nqb, int nkb,
+    int32_t *__restrict__ qcost) {
+  const int lane = threadIdx.x & 63;
+  const int qb = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), bh = blockIdx.y;
+  if (qb >= nqb) return;                       // wave-uniform; no barriers here
+  const size_t e = static_cast<size_t>(bh) * nqb + qb;
+  const int kc = kept_count[e];
+  const int32_t *kidx = kept_idx + e * kept_stride;
+  const int32_t *koff = k_off + static_cast<size_t>(bh) * (nkb + 1);
+  int L = 0;
+  for (int j = lane; j < kc; j += 64) {
+    const int b = kidx[j];
+    L += koff[b + 1] - koff[b];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+  if (lane == 0) qcost[e] = (L + kKT - 1) / kKT + kItemFixed;
+}
+
+__global__ __launch_bounds__(kThreads) void attn_schedule_kernel(
+    const int32_t *__restrict__ q_off, const int32_t *__restrict__ qcost, int nqb,
+    int work_cap, WorkItem *__restrict__ work, int32_t *__restrict__ hinfo) {
   __shared__ int32_t wsum[4];
+  __shared__ int32_t csum[4];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t *off = q_off + static_cast<size_t>(bh) * (nqb + 1);
   WorkItem *out = work + static_cast<size_t>(bh) * work_cap;
-  int base = 0;
+  int base = 0, cost_sum = 0;
   for (int b0 = 0; b0 < nqb; b0 += kThreads) {
     const int qb = b0 + t;
-    int tiles = 0;
-    if (qb < nqb) tiles = max(0, (off[qb + 1] - off[qb] + kQTile - 1) / kQTile);
-    int x = tiles;
+    int tiles = 0, cost = 0;
+    if (qb < nqb) {
+      tiles = max(0, (off[qb + 1] - off[qb] + kQTile - 1) / kQTile);
+      cost = qcost[static_cast<size_t>(bh) * nqb + qb];
+    }
+    int x = tiles, cs = tiles * cost;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o);
+      const int y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o);
     if (lane == 63) wsum[wave] = x;
+    if (lane == 0) csum[wave] = cs;
     __syncthreads();
     int pre = 0, total = 0;
     for (int w = 0; w < 4; ++w) {
       if (w < wave) pre += wsum[w];
       total += wsum[w];
+      cost_sum += t == 0 ? csum[w] : 0;
     }
     const int first = base + pre + x - tiles;
     for (int i = 0; i < tiles; ++i)
-      if (first + i < work_cap) out[first + i] = WorkItem{qb, i * kQTile};
+      if (first + i < work_cap) out[first + i] = WorkItem{bh, qb, i * kQTile, cost};
     base += total;
     __syncthreads();
   }
-  for (int i = base + t; i < work_cap; i += kThreads) out[i] = WorkItem{-1, -1};
+  for (int i = base + t; i < work_cap; i += kThreads) out[i] = WorkItem{bh, -1, -1, 0};
+  if (t == 0) {
+    hinfo[2 * bh] = cost_sum;
+    hinfo[2 * bh + 1] = min(base, work_cap);
+  }
+}
+
+__global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
+    const WorkItem *__restrict__ work, const int32_t *__restrict__ hinfo, int nbh, int work_cap,
+    WorkItem *__restrict__ lists, int32_t *__restrict__ ctl) {
+  __shared__ int32_t s_x[kMaxOrderHeads];            // XCD of each slice
+  __shared__ int32_t s_order[kMaxOrderHeads];        // slices by descending cost
+  __shared__ int32_t s_hist[8][kOrderBuckets];       // counts, then write cursors
+  __shared__ int32_t s_cnt[8], s_start[8];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const bool balance = nbh <= kMaxOrderHeads;
+  auto xcd_of = [&](int h) { return balance ? s_x[h] : (h & 7); };
+  for (int i = t; i < 8 * kOrderBuckets; i += kOrderThreads) (&s_hist[0][0])[i] = 0;
+  if (balance) {
+    // rank of each slice by (cost desc, index asc), then a greedy deal
+    for (int h = t; h < nbh; h += kOrderThreads) {
+      const int ch = hinfo[2 * h];
+      int r = 0;
+      for (int g = 0; g < nbh; ++g) {
+        const int cg = hinfo[2 * g];
+        r += (cg > ch || (cg == ch && g < h)) ? 1 : 0;
+      }
+      s_order[r] = h;
+    }
+    __syncthreads();
+    if (t == 0) {
+      long long load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int r = 0; r < nbh; ++r) {
+        const int h = s_order[r];
+        int best = 0;
+        for (int x = 1; x < 8; ++x) best = load[x] < load[best] ? x : best;
+        s_x[h] = best;
+        load[best] += hinfo[2 * h];
+      }
+    }
+  }
+  __syncthreads();
+  // histogram of item costs per XCD
+  const size_t total = static_cast<size_t>(nbh) * work_cap;
+  for (size_t i = t; i < total; i += kOrderThreads) {
+    const WorkItem it = work[i];
+    if (it.qb < 0) continue;
+    atomicAdd(&s_hist[xcd_of(it.bh)][min(it.cost, kOrderBuckets - 1)], 1);
+  }
+  __syncthreads();
+  // per XCD, exclusive scan in descending cost order (wave x scans XCD x)
+  if (wave < 8) {
+    constexpr int PER = kOrderBuckets / 64;
+    int v[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {           // lane's buckets, descending cost
+      v[j] = s_hist[wave][kOrderBuckets - 1 - (lane * PER + j)];
+      sum += v[j];
+    }
+    int x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    int run = x - sum;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      s_hist[wave][kOrderBuckets - 1 - (lane * PER + j)] = run;
+      run += v[j];
+    }
+    if (lane == 63) s_cnt[wave] = x;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int st = 0;
+    for (int x = 0; x < 8; ++x) {
+      s_start[x] = st;
+      st += s_cnt[x];
+    }
+  }
+  __syncthreads();
+  for (size_t i = t; i < total; i += kOrderThreads) {
+    const WorkItem it = work[i];
+    if (it.qb < 0) continue;
+    const int x = xcd_of(it.bh);
+    const int pos = atomicAdd(&s_hist[x][min(it.cost, kOrderBuckets - 1)], 1);
+    lists[s_start[x] + pos] = it;
+  }
+  if (t < 8) {
+    ctl[t] = s_cnt[t];
+    ctl[8 + t] = s_start[t];
+    ctl[16 + t] = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -173,8 +346,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     const uint16_t *__restrict__ v, void *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ q_off, const int32_t *__restrict__ k_off,
     const int32_t *__restrict__ kept_count, const int32_t *__restrict__ kept_idx,
-    int kept_stride, const WorkItem *__restrict__ work, int work_cap, int n_items, int n_q,
-    int n_k, int nqb, int nkb, int dense, float scale_log2) {
+    int kept_stride, const WorkItem *__restrict__ work, int work_cap, int n_items,
+    const WorkItem *__restrict__ lists, int32_t *__restrict__ ctl, int n_q, int n_k, int nqb,
+    int nkb, int dense, float scale_log2) {
   constexpr int PPR = D / 8;             // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;          // rows per 1 KB direct-to-LDS wave load
   constexpr int LPW = PPR / (kAttnThreads / 64);   // such loads per wave per tensor per chunk
@@ -192,12 +366,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   __shared__ int32_t sFlag[kKT];          // row-map scratch, all zero between uses
   __shared__ int32_t sWsum[kAttnThreads / 64];
 
-  int bh, qb, row0;
-  if (!decode_work(work, work_cap, n_items, dense, bh, qb, row0)) return;
+  __shared__ int32_t sNext;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   if (tid < kKT) sFlag[tid] = 0;          // ordered before first use by the setup barriers
+
+  // one work item: rows [row0, row0 + 256) of Q block qb of slice bh
+  auto item = [&](const int bh, const int qb, const int row0) {
   const int qs = dense ? 0 : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb];
   const int qe = dense ? n_q : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb + 1];
   const int rbase = qs + row0 + wave * kWaveRows;
@@ -491,6 +667,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       lse[static_cast<size_t>(bh) * n_q + myq[nt]] =
           l_tot > 0.f ? (m_run[nt] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
+  };
+
+  if (dense) {   // uniform items, one per workgroup
+    int bh, qb, row0;
+    if (!decode_work(work, work_cap, n_items, dense, bh, qb, row0)) return;
+    item(bh, qb, row0);
+    return;
+  }
+  // sparse: persistent workgroups over the per-XCD queues
+  int gone = 0;
+  for (;;) {
+    if (tid == 0) sNext = fetch_work(ctl, gone);
+    __syncthreads();
+    const int idx = sNext;
+    if (idx < 0) break;                   // uniform: every thread read the same value
+    const WorkItem it = lists[idx];
+    item(it.bh, it.qb, it.row0);
+    __syncthreads();                      // LDS and sNext are reused by the next item
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -555,13 +750,13 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
 }
 
 template <int D, bool OF>
-hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items, int grid,
-                    hipStream_t s) {
+hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items,
+                    const WorkItem *lists, int32_t *ctl, int grid, hipStream_t s) {
   hipLaunchKernelGGL((attn_bf16_kernel<D, OF>), dim3(grid), dim3(kAttnThreads), 0, s,
                      static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                      static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_off, a.k_off,
-                     a.kept_count, a.kept_idx, a.kept_stride, work, cap, n_items, a.n_q, a.n_k,
-                     a.nqb, a.nkb, a.dense, a.scale * kLog2e);
+                     a.kept_count, a.kept_idx, a.kept_stride, work, cap, n_items, lists, ctl,
+                     a.n_q, a.n_k, a.nqb, a.nkb, a.dense, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -576,36 +771,72 @@ hipError_t run_f32(const AttnArgs &a, const WorkItem *work, int cap, int n_items
   return hipGetLastError();
 }
 
+// compute units of the current device (the persistent grid), cached per device
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
 }  // namespace
 
 size_t attn_ws_bytes(int32_t bh, int32_t n_q, int32_t nqb) {
-  const size_t cap = static_cast<size_t>((n_q + kQTile - 1) / kQTile) + nqb;
-  return align_up(static_cast<size_t>(bh) * cap * sizeof(WorkItem), 256);
+  return sched_layout(bh, n_q, nqb).total;
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
   int cap;
   const WorkItem *work = nullptr;
+  const WorkItem *lists = nullptr;
+  int32_t *ctl = nullptr;
+  hipError_t e;
   if (a.dense) {
     cap = (a.n_q + kQTile - 1) / kQTile;
   } else {
     cap = (a.n_q + kQTile - 1) / kQTile + a.nqb;
-    WorkItem *w = static_cast<WorkItem *>(a.ws);
-    hipLaunchKernelGGL(attn_schedule_kernel, dim3(a.bh), dim3(kThreads), 0, s, a.q_off, a.nqb,
-                       cap, w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const SchedLayout L = sched_layout(a.bh, a.n_q, a.nqb);
+    char *ws = static_cast<char *>(a.ws);
+    WorkItem *w = reinterpret_cast<WorkItem *>(ws + L.items);
+    int32_t *qcost = reinterpret_cast<int32_t *>(ws + L.qcost);
+    int32_t *hinfo = reinterpret_cast<int32_t *>(ws + L.hinfo);
+    WorkItem *lst = reinterpret_cast<WorkItem *>(ws + L.lists);
+    ctl = reinterpret_cast<int32_t *>(ws + L.ctl);
+    hipLaunchKernelGGL(attn_cost_kernel,
+                       dim3((a.nqb + kThreads / 64 - 1) / (kThreads / 64), a.bh), dim3(kThreads),
+                       0, s, a.k_off, a.kept_count, a.kept_idx, a.kept_stride, a.nqb, a.nkb,
+                       qcost);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(a.bh), dim3(kThreads), 0, s, a.q_off, qcost,
+                       a.nqb, cap, w, hinfo);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.dtype == SVA_BF16) {
+      hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, w, hinfo, a.bh,
+                         cap, lst, ctl);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     work = w;
+    lists = lst;
   }
   const long long n_items = static_cast<long long>(a.bh) * cap;
   const long long grid = (n_items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const bool of = a.o_dtype == SVA_F32;
   if (a.dtype == SVA_BF16) {
-    if (a.d == 128) return of ? run_bf16<128, true>(a, work, cap, (int)n_items, (int)grid, s)
-                              : run_bf16<128, false>(a, work, cap, (int)n_items, (int)grid, s);
-    return of ? run_bf16<64, true>(a, work, cap, (int)n_items, (int)grid, s)
-              : run_bf16<64, false>(a, work, cap, (int)n_items, (int)grid, s);
+    // dense: one workgroup per item; sparse: one persistent workgroup per compute unit
+    // (one fits per CU), at most one per item
+    const int g = a.dense ? static_cast<int>(grid)
+                          : static_cast<int>(std::min<long long>(device_cus(), grid));
+    if (a.d == 128) return of ? run_bf16<128, true>(a, work, cap, (int)n_items, lists, ctl, g, s)
+                              : run_bf16<128, false>(a, work, cap, (int)n_items, lists, ctl, g, s);
+    return of ? run_bf16<64, true>(a, work, cap, (int)n_items, lists, ctl, g, s)
+              : run_bf16<64, false>(a, work, cap, (int)n_items, lists, ctl, g, s);
   }
   if (a.d == 128) return of ? run_f32<128, true>(a, work, cap, (int)n_items, (int)grid, s)
                             : run_f32<128, false>(a, work, cap, (int)n_items, (int)grid, s);
