@@ -4,9 +4,11 @@ Workload (default): the 5 s clip layer -- 32,760 latent tokens (21x30x52 grid)
 x 40 heads, d=128, bf16; k-means with C_q=100 / C_k=500 for 10 iterations,
 top-p 0.9; seeded synthetic mixture-of-Gaussians tokens (centre scale 1.75,
 about 85% sparsity).  A step is one pass of the whole hot path: k-means of Q
-and of K, permutation of Q and of K/V (the Q side on a second stream,
-concurrently with the K/V side), top-p selection, block-sparse attention,
-unpermutation.  Inputs are resident in HBM before timing.
+and of K, the cluster sort of Q and of K (the Q side on a second stream,
+concurrently with the K side), top-p selection, block-sparse attention that
+reads Q/K/V through the permutation and writes O in token order (``--unfused``:
+gather the permuted Q/K/V, attend, unpermute O).  Inputs are resident in HBM
+before timing.
 
 Prints one JSON line: value = effective TFLOP/s of the layer (4 d x kept
 (query, key) pairs per step / step time), ms_per_step = ms per layer, plus the
@@ -91,6 +93,9 @@ def main() -> int:
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="materialise the permuted Q/K/V and unpermute O (instead of reading "
+                         "and writing through the permutation inside attention)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run 3 identity-permutation copies of Q (335.5 MB read + "
                          "335.5 MB written at 5 s) to calibrate HBM byte counters")
@@ -119,7 +124,7 @@ def main() -> int:
     ik = torch.from_numpy(init_k).to(dev)
     del x
     layer = SparseVideoAttention(cfg.batch, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
-                                 cfg.top_p, device=dev)
+                                 cfg.top_p, device=dev, fuse_permutation=not args.unfused)
     # "cluster" = k-means + permutation of Q (side stream) and of K/V, joined
     stages = ("cluster", "select", "attention", "unpermute")
 
@@ -132,7 +137,7 @@ def main() -> int:
         layer.select()
         if ev is not None:
             ev[2].record()
-        layer.attend()
+        layer.attend(t["q"], t["k"], t["v"])
         if ev is not None:
             ev[3].record()
         layer.unpermute()
@@ -216,7 +221,8 @@ def main() -> int:
         "config": {"workload": f"svg2 sparse attention layer, {cfg.name} clip",
                    "tokens": cfg.n, "grid_thw": [cfg.T, cfg.H, cfg.W], "heads": cfg.heads,
                    "head_dim": cfg.d, "batch": cfg.batch, "cq": cfg.cq, "ck": cfg.ck,
-                   "kmeans_iters": cfg.iters, "top_p": cfg.top_p, "centre_scale": cfg.alpha,
+                   "kmeans_iters": cfg.iters, "top_p": cfg.top_p,
+                   "fused_permutation": not args.unfused, "centre_scale": cfg.alpha,
                    "density": round(density, 5), "kept_pairs": kept},
         "ms_per_layer": round(ms_step, 4),
         "frac_of_peak_layer": round(value / PEAK_BF16_TFLOPS, 5),

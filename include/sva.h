@@ -167,6 +167,31 @@ int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32
                               int32_t kept_stride, float scale, void *o, int32_t o_dtype,
                               float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * sva_block_sparse_attn_perm -- the same attention with the permutation
+ * fused into its loads and stores (Sparse VideoGen2, section 2.a: the
+ * permutation only makes each cluster contiguous; section 2.c: sparse loading
+ * of the kept K/V).  q, k, v, o and lse stay in ORIGINAL token order; the
+ * blocks are ranges of the PERMUTED order, as sva_permute returns them:
+ *
+ *   q_perm     [bh][n_q] int32: q_perm[i] = original row of permuted query
+ *              row i (a permutation of [0, n_q); device precondition)
+ *   k_perm     [bh][n_k] int32: likewise for the key/value rows
+ *
+ * Every other argument is as for sva_block_sparse_attn.  The result equals
+ * sva_block_sparse_attn on the gathered tensors q[q_perm], k[k_perm],
+ * v[k_perm] followed by sva_unpermute, bit for bit; it writes o and lse at
+ * the original rows, and skips both gathers and the unpermutation.
+ * ------------------------------------------------------------------------ */
+int32_t sva_block_sparse_attn_perm(const void *q, const void *k, const void *v, int32_t dtype,
+                                   int32_t batch, int32_t heads, int32_t n_q, int32_t n_k,
+                                   int32_t d, const int32_t *q_perm, const int32_t *k_perm,
+                                   const int32_t *q_offsets, int32_t n_qblocks,
+                                   const int32_t *k_offsets, int32_t n_kblocks,
+                                   const int32_t *kept_count, const int32_t *kept_idx,
+                                   int32_t kept_stride, float scale, void *o, int32_t o_dtype,
+                                   float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * sva_unpermute -- o[perm[i]] = o_perm[i] per slice (Sparse VideoGen2,
  * section 2.a: the permuted result is mapped back to token order).

@@ -7,7 +7,7 @@ call does, and raises if it has not been built.
 """
 from ._lib import (  # noqa: F401
     SVA_BF16, SVA_F32, LIB_PATH, lib, last_error,
-    sva_kmeans, sva_permute, sva_select_blocks, sva_block_sparse_attn, sva_unpermute,
-    sva_full_attn,
+    sva_kmeans, sva_permute, sva_select_blocks, sva_block_sparse_attn,
+    sva_block_sparse_attn_perm, sva_unpermute, sva_full_attn,
 )
 from .layer import SparseVideoAttention  # noqa: F401

@@ -40,6 +40,8 @@ SIGNATURES = {
     "sva_attn_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "sva_block_sparse_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P,
                                    _I, _F, _P, _I, _P, _P, _Z, _P]),
+    "sva_block_sparse_attn_perm": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P,
+                                        _I, _P, _P, _I, _F, _P, _I, _P, _P, _Z, _P]),
     "sva_unpermute": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "sva_full_attn_workspace_bytes": (_Z, [_I, _I, _I]),
     "sva_full_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _Z, _P]),
@@ -193,6 +195,33 @@ def sva_block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                        _ptr(kept_count), _ptr(kept_idx), kept_idx.shape[-1],
                                        float(scale), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(w),
                                        wb, _stream(q)), "sva_block_sparse_attn")
+    return o, lse
+
+
+def sva_block_sparse_attn_perm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               q_perm: torch.Tensor, k_perm: torch.Tensor,
+                               q_offsets: torch.Tensor, k_offsets: torch.Tensor,
+                               kept_count: torch.Tensor, kept_idx: torch.Tensor, scale: float,
+                               o: Optional[torch.Tensor] = None, o_dtype=None,
+                               lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                               ws: Optional[torch.Tensor] = None):
+    """Attention over the kept blocks with the permutation fused in: q, k, v, o, lse in
+    original token order, blocks over the permuted order.  Returns (o, lse or None)."""
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    nqb = q_offsets.shape[-1] - 1
+    nkb = k_offsets.shape[-1] - 1
+    if o is None:
+        o = torch.empty((b, h, nq, d), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+    need = lib().sva_attn_workspace_bytes(b, h, nq, nqb)
+    w, wb = _workspace(need, q, ws)
+    _check(lib().sva_block_sparse_attn_perm(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), b, h, nq, nk, d, _ptr(q_perm), _ptr(k_perm),
+        _ptr(q_offsets), nqb, _ptr(k_offsets), nkb, _ptr(kept_count), _ptr(kept_idx),
+        kept_idx.shape[-1], float(scale), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(w), wb,
+        _stream(q)), "sva_block_sparse_attn_perm")
     return o, lse
 
 

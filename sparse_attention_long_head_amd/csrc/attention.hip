@@ -340,10 +340,11 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention
 // ---------------------------------------------------------------------------
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool PERM>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, void *__restrict__ o, float *__restrict__ lse,
+    const int32_t *__restrict__ q_perm, const int32_t *__restrict__ k_perm,
     const int32_t *__restrict__ q_off, const int32_t *__restrict__ k_off,
     const int32_t *__restrict__ kept_count, const int32_t *__restrict__ kept_idx,
     int kept_stride, const WorkItem *__restrict__ work, int work_cap, int n_items,
@@ -363,6 +364,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   __shared__ int32_t sStart[kLCap];
   __shared__ int32_t sCum[kLCap + 1];
   __shared__ int32_t sRow[kStages][kKT];
+  __shared__ int32_t sPerm[kStages][kKT];  // PERM: original row of each chunk key
   __shared__ int32_t sFlag[kKT];          // row-map scratch, all zero between uses
   __shared__ int32_t sWsum[kAttnThreads / 64];
 
@@ -388,12 +390,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     qvalid[nt] = myq[nt] < qe;
   }
 
-  // Q fragments: lane holds Q[myq][16 s + 8 h .. +8] (B operand of S^T = K Q^T)
+  // source row of each lane's query: the permuted row itself, or (PERM) its
+  // original row, which is also where its output goes
+  int qrow_id[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if constexpr (PERM) qrow_id[nt] = qvalid[nt] ? q_perm[static_cast<size_t>(bh) * n_q + myq[nt]] : 0;
+    else qrow_id[nt] = qvalid[nt] ? myq[nt] : 0;
+  }
+  // Q fragments: lane holds Q[query][16 s + 8 h .. +8] (B operand of S^T = K Q^T)
   bf16x8 qf[NT][NS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t *qrow =
-        q + (static_cast<size_t>(bh) * n_q + (qvalid[nt] ? myq[nt] : 0)) * D + h * 8;
+    const uint16_t *qrow = q + (static_cast<size_t>(bh) * n_q + qrow_id[nt]) * D + h * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4 raw = qvalid[nt] ? *reinterpret_cast<const u32x4 *>(qrow + s * 16) : u32x4{0, 0, 0, 0};
@@ -417,6 +426,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   const int32_t *kidx = kept_idx + (static_cast<size_t>(bh) * nqb + qb) * kept_stride;
   const int32_t *koff = k_off + static_cast<size_t>(bh) * (nkb + 1);
   const uint16_t *kbase = k + static_cast<size_t>(bh) * n_k * D;
+  const int32_t *pbase = PERM ? k_perm + static_cast<size_t>(bh) * n_k : nullptr;
   const uint16_t *vbase = v + static_cast<size_t>(bh) * n_k * D;
 
   // Direct-to-LDS load geometry: wave load j writes LDS bytes [1 KB * (wave*LPW + j), +1 KB):
@@ -492,7 +502,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     // chunk marks its position, and a ballot of the marks gives every lane the
     // number of range starts at or before its key, hence its range.
     int jcur = 0;
-    auto rowmap = [&](int c, int32_t *dst) {
+    auto rowmap = [&](int c, auto st) {
+      int32_t *dst = sRow[decltype(st)::value];
       if (wave == 0) {
         const int c0 = c * kKT;
         const int jb = jcur + 1 + lane;
@@ -503,8 +514,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
         if (mark) sFlag[p] = 0;
         const int seg = jcur + __popcll(starts & ((2ull << lane) - 1));
         const int vv = c0 + lane;
-        dst[lane] = vv < L ? sStart[seg] + (vv - sCum[seg]) : -1;
+        const int rr = vv < L ? sStart[seg] + (vv - sCum[seg]) : -1;
+        dst[lane] = rr;
         jcur += __popcll(__ballot(p <= kKT));     // the range holding key c0 + 64
+        if constexpr (PERM) {   // original rows: copied HBM -> LDS like the K/V rows
+          const int32_t *src = pbase + (rr < 0 ? 0 : rr);
+          __builtin_amdgcn_global_load_lds(
+              src, (__attribute__((address_space(3))) void *)&sPerm[decltype(st)::value][0], 4, 0, 0);
+        }
       }
     };
     // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
@@ -514,12 +531,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       uint16_t *dv = sV[decltype(st)::value];
       // past the end of the list (the two chunks after the last) whole stages are
       // refilled from key row 0, so every step issues the same number of copies
-      const int dummy = max(rows[0], 0);
+      int dummy = max(rows[0], 0);
+      int prow[LPW];
+      if constexpr (PERM) {   // original rows of this lane's keys (and of key 0)
+        const uint32_t pb = lds_offset(&sPerm[decltype(st)::value][0]);
+        uint32_t pa[LPW + 1];
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) pa[j] = pb + 4 * (RPI * (wave * LPW + j) + ld_rsub);
+        pa[LPW] = pb;
+        int pv[LPW + 1];
+        lds_read_i32s(pv, pa);
+        dummy = rows[0] < 0 ? 0 : pv[LPW];
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) prow[j] = pv[j];
+      }
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int blk = wave * LPW + j;
         const int r = RPI * blk + ld_rsub;
         int phys = rows[r];
+        if constexpr (PERM) phys = phys < 0 ? -1 : prow[j];
         phys = phys < 0 ? dummy : phys;
         // (offsets stay in named variables: with an arithmetic expression in the
         // builtin's argument list, hipcc 7.2's host pass emits no launch stub)
@@ -536,9 +567,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
 
     // prologue: chunks 0 and 1 in flight, row map of chunk 2 ready (a row map
     // past the end of the list is all -1)
-    rowmap(0, sRow[0]);
-    rowmap(1, sRow[1]);
-    rowmap(2, sRow[2]);
+    rowmap(0, std::integral_constant<int, 0>{});
+    rowmap(1, std::integral_constant<int, 1>{});
+    rowmap(2, std::integral_constant<int, 2>{});
+    if constexpr (PERM) wait_vmcnt<1>();   // original rows of chunks 0, 1 landed (wave 0)
     lds_barrier();
     issue_loads(std::integral_constant<int, 0>{});
     issue_loads(std::integral_constant<int, 1>{});
@@ -549,10 +581,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       // chunk c has landed once only chunk c+1's copies are outstanding; after
       // the barrier every wave's copies of chunk c are in LDS and every wave is
       // done with chunk c-1, whose stage chunk c+2 then refills
+      // (PERM: wave 0's copy of the original rows of chunk c+2 is older than
+      // chunk c+1's K/V copies, so it has landed too)
       wait_vmcnt<2 * LPW>();
       lds_barrier();
+      rowmap(c + 3, std::integral_constant<int, S>{});
       issue_loads(std::integral_constant<int, (S + 2) % 3>{});
-      rowmap(c + 3, sRow[S]);
 
       if (wave_active) {
         // S^T = K Q^T for 64 keys (two 32-key m-tiles) x the wave's query tiles;
@@ -648,7 +682,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (!qvalid[nt]) continue;
-    const size_t orow = (static_cast<size_t>(bh) * n_q + myq[nt]) * D;
+    const size_t orow = (static_cast<size_t>(bh) * n_q + qrow_id[nt]) * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -664,7 +698,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
         }
       }
     if (h == 0 && lse != nullptr)
-      lse[static_cast<size_t>(bh) * n_q + myq[nt]] =
+      lse[static_cast<size_t>(bh) * n_q + qrow_id[nt]] =
           l_tot > 0.f ? (m_run[nt] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
   };
@@ -694,7 +728,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    void *__restrict__ o, float *__restrict__ lse, const int32_t *__restrict__ q_off,
+    void *__restrict__ o, float *__restrict__ lse, const int32_t *__restrict__ q_perm,
+    const int32_t *__restrict__ k_perm, const int32_t *__restrict__ q_off,
     const int32_t *__restrict__ k_off, const int32_t *__restrict__ kept_count,
     const int32_t *__restrict__ kept_idx, int kept_stride, const WorkItem *__restrict__ work,
     int work_cap, int n_items, int n_q, int n_k, int nqb, int nkb, int dense, float scale) {
@@ -705,7 +740,10 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
   const int myq = qs + row0 + threadIdx.x;
   const bool qvalid = myq < qe;
   float qv[D], acc[D];
-  const float *qrow = q + (static_cast<size_t>(bh) * n_q + (qvalid ? myq : qs)) * D;
+  // q_perm / k_perm (may be NULL): permuted row -> original row of q, o, lse / of k, v
+  const int qrow_id = q_perm == nullptr ? (qvalid ? myq : qs)
+                                        : q_perm[static_cast<size_t>(bh) * n_q + (qvalid ? myq : qs)];
+  const float *qrow = q + (static_cast<size_t>(bh) * n_q + qrow_id) * D;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     qv[i] = qvalid ? qrow[i] : 0.f;
@@ -723,8 +761,9 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
       en = koff[b + 1];
     }
     for (int key = st; key < en; ++key) {
-      const float *kr = k + (static_cast<size_t>(bh) * n_k + key) * D;
-      const float *vr = v + (static_cast<size_t>(bh) * n_k + key) * D;
+      const int kr_id = k_perm == nullptr ? key : k_perm[static_cast<size_t>(bh) * n_k + key];
+      const float *kr = k + (static_cast<size_t>(bh) * n_k + kr_id) * D;
+      const float *vr = v + (static_cast<size_t>(bh) * n_k + kr_id) * D;
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < D; ++i) s = fmaf(qv[i], kr[i], s);
@@ -740,21 +779,31 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
   }
   if (!qvalid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const size_t orow = (static_cast<size_t>(bh) * n_q + myq) * D;
+  const size_t orow = (static_cast<size_t>(bh) * n_q + qrow_id) * D;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     if constexpr (OUT_F32) static_cast<float *>(o)[orow + i] = acc[i] * inv;
     else static_cast<uint16_t *>(o)[orow + i] = f32_to_bf16_bits(acc[i] * inv);
   }
-  if (lse != nullptr) lse[static_cast<size_t>(bh) * n_q + myq] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (lse != nullptr) lse[static_cast<size_t>(bh) * n_q + qrow_id] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 template <int D, bool OF>
 hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items,
                     const WorkItem *lists, int32_t *ctl, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, OF>), dim3(grid), dim3(kAttnThreads), 0, s,
+  if (a.q_perm != nullptr) {
+    hipLaunchKernelGGL((attn_bf16_kernel<D, OF, true>), dim3(grid), dim3(kAttnThreads), 0, s,
+                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+                       static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_perm, a.k_perm,
+                       a.q_off, a.k_off, a.kept_count, a.kept_idx, a.kept_stride, work, cap,
+                       n_items, lists, ctl, a.n_q, a.n_k, a.nqb, a.nkb, a.dense,
+                       a.scale * kLog2e);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn_bf16_kernel<D, OF, false>), dim3(grid), dim3(kAttnThreads), 0, s,
                      static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                     static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_off, a.k_off,
+                     static_cast<const uint16_t *>(a.v), a.o, a.lse, nullptr, nullptr, a.q_off,
+                     a.k_off,
                      a.kept_count, a.kept_idx, a.kept_stride, work, cap, n_items, lists, ctl,
                      a.n_q, a.n_k, a.nqb, a.nkb, a.dense, a.scale * kLog2e);
   return hipGetLastError();
@@ -765,7 +814,8 @@ hipError_t run_f32(const AttnArgs &a, const WorkItem *work, int cap, int n_items
                    hipStream_t s) {
   hipLaunchKernelGGL((attn_f32_kernel<D, OF>), dim3(grid), dim3(kQTile), 0, s,
                      static_cast<const float *>(a.q), static_cast<const float *>(a.k),
-                     static_cast<const float *>(a.v), a.o, a.lse, a.q_off, a.k_off, a.kept_count,
+                     static_cast<const float *>(a.v), a.o, a.lse, a.q_perm, a.k_perm, a.q_off,
+                     a.k_off, a.kept_count,
                      a.kept_idx, a.kept_stride, work, cap, n_items, a.n_q, a.n_k, a.nqb, a.nkb,
                      a.dense, a.scale);
   return hipGetLastError();

@@ -128,4 +128,28 @@ __device__ __forceinline__ void lds_read_f32x4x4(f32x4 (&f)[4], uint32_t a) {
       : "memory");
 }
 
+// N ds_read_b32 (N = 2 or 3) at per-lane byte addresses a[i]; waits for them.
+template <int N>
+__device__ __forceinline__ void lds_read_i32s(int (&v)[N], const uint32_t (&a)[N]) {
+  if constexpr (N == 3) {
+    asm volatile(
+        "ds_read_b32 %0, %3\n\t"
+        "ds_read_b32 %1, %4\n\t"
+        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2])
+        : "memory");
+  } else {
+    static_assert(N == 2, "2 or 3 reads");
+    asm volatile(
+        "ds_read_b32 %0, %2\n\t"
+        "ds_read_b32 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+  }
+}
+
 }  // namespace sva

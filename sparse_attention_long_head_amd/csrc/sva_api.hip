@@ -176,14 +176,14 @@ size_t sva_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q, int32
   return sva::attn_ws_bytes(batch * heads, n_q, n_qblocks);
 }
 
-int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32_t dtype,
-                              int32_t batch, int32_t heads, int32_t n_q, int32_t n_k, int32_t d,
-                              const int32_t *q_offsets, int32_t n_qblocks,
-                              const int32_t *k_offsets, int32_t n_kblocks,
-                              const int32_t *kept_count, const int32_t *kept_idx,
-                              int32_t kept_stride, float scale, void *o, int32_t o_dtype,
-                              float *lse, void *ws, size_t ws_bytes, void *stream) {
-  const char *fn = "sva_block_sparse_attn";
+static int32_t block_sparse(const char *fn, const void *q, const void *k, const void *v,
+                            int32_t dtype, int32_t batch, int32_t heads, int32_t n_q, int32_t n_k,
+                            int32_t d, const int32_t *q_perm, const int32_t *k_perm,
+                            const int32_t *q_offsets, int32_t n_qblocks,
+                            const int32_t *k_offsets, int32_t n_kblocks,
+                            const int32_t *kept_count, const int32_t *kept_idx,
+                            int32_t kept_stride, float scale, void *o, int32_t o_dtype,
+                            float *lse, void *ws, size_t ws_bytes, void *stream) {
   SVA_TRY(check_attn(fn, q, k, v, dtype, batch, heads, n_q, n_k, d, scale, o, o_dtype));
   if (!q_offsets || !k_offsets || !kept_count || !kept_idx)
     return fail(SVA_EINVAL, "%s: offsets and kept lists must be non-NULL", fn);
@@ -195,9 +195,37 @@ int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32
   const long long items = static_cast<long long>(batch) * heads * ((n_q + 127) / 128 + n_qblocks);
   if (items > 0x7ffffff0LL) return fail(SVA_EUNSUPPORTED, "%s: problem too large for one launch", fn);
   SVA_TRY(check_ws(fn, sva::attn_ws_bytes(batch * heads, n_q, n_qblocks), ws, ws_bytes));
-  sva::AttnArgs a{q, k, v, o, lse, q_offsets, k_offsets, kept_count, kept_idx, kept_stride,
-                  batch * heads, n_q, n_k, d, n_qblocks, n_kblocks, dtype, o_dtype, 0, scale, ws};
+  sva::AttnArgs a{q, k, v, o, lse, q_offsets, k_offsets, kept_count, kept_idx, q_perm, k_perm,
+                  kept_stride, batch * heads, n_q, n_k, d, n_qblocks, n_kblocks, dtype, o_dtype,
+                  0, scale, ws};
   return hip_status(sva::launch_attention(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32_t dtype,
+                              int32_t batch, int32_t heads, int32_t n_q, int32_t n_k, int32_t d,
+                              const int32_t *q_offsets, int32_t n_qblocks,
+                              const int32_t *k_offsets, int32_t n_kblocks,
+                              const int32_t *kept_count, const int32_t *kept_idx,
+                              int32_t kept_stride, float scale, void *o, int32_t o_dtype,
+                              float *lse, void *ws, size_t ws_bytes, void *stream) {
+  return block_sparse("sva_block_sparse_attn", q, k, v, dtype, batch, heads, n_q, n_k, d,
+                      nullptr, nullptr, q_offsets, n_qblocks, k_offsets, n_kblocks, kept_count,
+                      kept_idx, kept_stride, scale, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int32_t sva_block_sparse_attn_perm(const void *q, const void *k, const void *v, int32_t dtype,
+                                   int32_t batch, int32_t heads, int32_t n_q, int32_t n_k,
+                                   int32_t d, const int32_t *q_perm, const int32_t *k_perm,
+                                   const int32_t *q_offsets, int32_t n_qblocks,
+                                   const int32_t *k_offsets, int32_t n_kblocks,
+                                   const int32_t *kept_count, const int32_t *kept_idx,
+                                   int32_t kept_stride, float scale, void *o, int32_t o_dtype,
+                                   float *lse, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "sva_block_sparse_attn_perm";
+  if (!q_perm || !k_perm) return fail(SVA_EINVAL, "%s: q_perm and k_perm must be non-NULL", fn);
+  return block_sparse(fn, q, k, v, dtype, batch, heads, n_q, n_k, d, q_perm, k_perm, q_offsets,
+                      n_qblocks, k_offsets, n_kblocks, kept_count, kept_idx, kept_stride, scale,
+                      o, o_dtype, lse, ws, ws_bytes, stream);
 }
 
 size_t sva_full_attn_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
@@ -209,7 +237,7 @@ int32_t sva_full_attn(const void *q, const void *k, const void *v, int32_t dtype
   (void)ws;
   (void)ws_bytes;
   SVA_TRY(check_attn(fn, q, k, v, dtype, batch, heads, n_q, n_k, d, scale, o, o_dtype));
-  sva::AttnArgs a{q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, 0,
+  sva::AttnArgs a{q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                   batch * heads, n_q, n_k, d, 1, 1, dtype, o_dtype, 1, scale, nullptr};
   return hip_status(sva::launch_attention(a, static_cast<hipStream_t>(stream)), fn);
 }

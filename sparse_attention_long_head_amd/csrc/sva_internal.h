@@ -54,6 +54,7 @@ struct AttnArgs {
   void *o;
   float *lse;
   const int32_t *q_off, *k_off, *kept_count, *kept_idx;
+  const int32_t *q_perm, *k_perm;   // NULL, or permuted row -> original row (fused permutation)
   int32_t kept_stride;
   int32_t bh, n_q, n_k, d, nqb, nkb;
   int32_t dtype, o_dtype;     // SVA_F32 / SVA_BF16

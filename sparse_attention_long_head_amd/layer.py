@@ -4,6 +4,12 @@ Sparse VideoGen2 explainer, technical summary section 2: k-means of Q and K
 (2.a), permutation so that clusters are contiguous (2.a), centroid top-p
 (2.b), attention over the kept blocks (2.c), inverse permutation (2.a).
 
+With ``fuse_permutation`` (the default) the permutation never materialises:
+the sort only produces the permutation and the block offsets, and the
+attention kernel reads Q, K and V rows through the permutation and writes O
+(and the LSE) back to the original token order, so there is no gather of Q, K,
+V and no unpermute pass.  The result equals the unfused sequence bit for bit.
+
 ``SparseVideoAttention`` owns every buffer the layer needs (allocated once,
 through torch), so ``forward`` only enqueues the library calls: it allocates
 nothing and never synchronises.  The clustering and permutation of Q run on a
@@ -26,8 +32,10 @@ from . import _lib as L
 class SparseVideoAttention:
     def __init__(self, batch: int, heads: int, n: int, d: int, cq: int, ck: int, iters: int,
                  top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda",
-                 scale: Optional[float] = None, want_lse: bool = False):
+                 scale: Optional[float] = None, want_lse: bool = False,
+                 fuse_permutation: bool = True):
         self.shape = (batch, heads, n, d)
+        self.fused = fuse_permutation
         self.cq, self.ck, self.iters, self.top_p = cq, ck, iters, top_p
         # a float32-representable scale, so the fp64 selection and the fp32
         # attention kernels use the identical value
@@ -45,16 +53,17 @@ class SparseVideoAttention:
         self.perm_k = torch.empty((batch, heads, n), **i32)
         self.off_q = torch.empty((batch, heads, cq + 1), **i32)
         self.off_k = torch.empty((batch, heads, ck + 1), **i32)
-        self.q_p = torch.empty(self.shape, dtype=dtype, device=dev)
-        self.k_p = torch.empty(self.shape, dtype=dtype, device=dev)
-        self.v_p = torch.empty(self.shape, dtype=dtype, device=dev)
+        # cluster-ordered copies of Q, K, V and O: only the unfused path has them
+        perm_buf = (lambda: None) if self.fused else (
+            lambda: torch.empty(self.shape, dtype=dtype, device=dev))
+        self.q_p, self.k_p, self.v_p, self.o_p = perm_buf(), perm_buf(), perm_buf(), perm_buf()
         self.mask = torch.empty((batch, heads, cq, ck), dtype=torch.uint8, device=dev)
         self.kept_count = torch.empty((batch, heads, cq), **i32)
         self.kept_idx = torch.empty((batch, heads, cq, ck), **i32)
-        self.o_p = torch.empty(self.shape, dtype=dtype, device=dev)
         self.o = torch.empty(self.shape, dtype=dtype, device=dev)
-        # LSE of the permuted query rows (row i belongs to token perm_q[i])
-        self.lse_p = torch.empty((batch, heads, n), **f32) if want_lse else None
+        # LSE per query row: in original token order when fused, else of the
+        # permuted rows (row i belongs to token perm_q[i])
+        self.lse = torch.empty((batch, heads, n), **f32) if want_lse else None
         lib = L.lib()
         km = max(lib.sva_kmeans_workspace_bytes(batch, heads, n, d, cq),
                  lib.sva_kmeans_workspace_bytes(batch, heads, n, d, ck))
@@ -73,22 +82,40 @@ class SparseVideoAttention:
         L.sva_kmeans(q, self.cq, self.iters, self.cent_q, self.assign_q, self.sizes_q, ws=self.ws)
         L.sva_kmeans(k, self.ck, self.iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
 
+    def _sort_q(self, q, ws):
+        L.sva_permute(self.assign_q, self.cq, [] if self.fused else [q], self.perm_q, self.off_q,
+                      None if self.fused else [self.q_p], ws=ws)
+
+    def _sort_kv(self, k, v, ws):
+        L.sva_permute(self.assign_k, self.ck, [] if self.fused else [k, v], self.perm_k,
+                      self.off_k, None if self.fused else [self.k_p, self.v_p], ws=ws)
+
     def permute(self, q, k, v):
-        L.sva_permute(self.assign_q, self.cq, [q], self.perm_q, self.off_q, [self.q_p], ws=self.ws)
-        L.sva_permute(self.assign_k, self.ck, [k, v], self.perm_k, self.off_k,
-                      [self.k_p, self.v_p], ws=self.ws)
+        self._sort_q(q, self.ws)
+        self._sort_kv(k, v, self.ws)
 
     def select(self):
         L.sva_select_blocks(self.cent_q, self.sizes_q, self.cent_k, self.sizes_k, self.scale,
                             self.top_p, self.mask, self.kept_count, self.kept_idx)
 
-    def attend(self):
-        L.sva_block_sparse_attn(self.q_p, self.k_p, self.v_p, self.off_q, self.off_k,
-                                self.kept_count, self.kept_idx, self.scale, o=self.o_p,
-                                lse=self.lse_p, ws=self.ws)
+    def attend(self, q=None, k=None, v=None):
+        """Attention over the kept blocks; the fused path needs the original
+        q, k, v (the unfused one reads its permuted copies)."""
+        if self.fused:
+            if q is None or k is None or v is None:
+                raise ValueError("attend: the fused path needs the original q, k and v")
+            L.sva_block_sparse_attn_perm(q, k, v, self.perm_q, self.perm_k, self.off_q,
+                                         self.off_k, self.kept_count, self.kept_idx, self.scale,
+                                         o=self.o, lse=self.lse, ws=self.ws)
+        else:
+            L.sva_block_sparse_attn(self.q_p, self.k_p, self.v_p, self.off_q, self.off_k,
+                                    self.kept_count, self.kept_idx, self.scale, o=self.o_p,
+                                    lse=self.lse, ws=self.ws)
 
     def unpermute(self):
-        L.sva_unpermute(self.o_p, self.perm_q, self.o)
+        """Inverse permutation of the output (nothing to do when fused)."""
+        if not self.fused:
+            L.sva_unpermute(self.o_p, self.perm_q, self.o)
 
     def cluster(self, q, k, v, init_q, init_k):
         """k-means and permutation of Q (side stream) and of K, V (current
@@ -100,18 +127,16 @@ class SparseVideoAttention:
             self.cent_q.copy_(init_q)
             L.sva_kmeans(q, self.cq, self.iters, self.cent_q, self.assign_q, self.sizes_q,
                          ws=self.ws_q)
-            L.sva_permute(self.assign_q, self.cq, [q], self.perm_q, self.off_q, [self.q_p],
-                          ws=self.ws_q)
+            self._sort_q(q, self.ws_q)
         self.cent_k.copy_(init_k)
         L.sva_kmeans(k, self.ck, self.iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
-        L.sva_permute(self.assign_k, self.ck, [k, v], self.perm_k, self.off_k,
-                      [self.k_p, self.v_p], ws=self.ws)
+        self._sort_kv(k, v, self.ws)
         cur.wait_stream(self.side)
 
     def forward(self, q, k, v, init_q, init_k) -> torch.Tensor:
         self.cluster(q, k, v, init_q, init_k)
         self.select()
-        self.attend()
+        self.attend(q, k, v)
         self.unpermute()
         return self.o
 

@@ -17,7 +17,8 @@ import torch
 import oracle
 import synth
 from parity import (check_attention, check_lse, device, host, rand_inputs, to_dev)
-from sparse_attention_long_head_amd import sva_block_sparse_attn, sva_full_attn
+from sparse_attention_long_head_amd import (sva_block_sparse_attn, sva_block_sparse_attn_perm,
+                                          sva_full_attn)
 
 pytestmark = pytest.mark.gpu
 
@@ -244,3 +245,50 @@ def test_dense_full_size_sampled(static_full):
         ro, _ = oracle.full_attention(x["q"][0, h], x["k"][0, h], x["v"][0, h],
                                       np.float32(scale), rows=rows)
         check_attention(o[0, h, rows], ro, True, f"dense head {h}")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_permutation_equals_gather_attend_scatter(bf16, d):
+    # sva_block_sparse_attn_perm on original-order tensors must equal, bit for
+    # bit, gathering q[q_perm], k[k_perm], v[k_perm], sva_block_sparse_attn and
+    # scattering the output back; and it must match the oracle in original
+    # coordinates
+    rng = np.random.default_rng(7 + d)
+    heads, nq, nk, nqb, nkb = 2, 701, 866, 11, 29
+    dt = "bf16" if bf16 else "f32"
+    q = rand_inputs((1, heads, nq, d), 70, dt)
+    k = rand_inputs((1, heads, nk, d), 71, dt)
+    v = rand_inputs((1, heads, nk, d), 72, dt)
+    qoff = np.stack([_random_partition(nq, nqb, rng) for _ in range(heads)])[None]
+    koff = np.stack([_random_partition(nk, nkb, rng) for _ in range(heads)])[None]
+    qperm = np.stack([rng.permutation(nq) for _ in range(heads)])[None].astype(np.int32)
+    kperm = np.stack([rng.permutation(nk) for _ in range(heads)])[None].astype(np.int32)
+    masks = rng.random((1, heads, nqb, nkb)) < 0.4
+    cnt, idx = synth.mask_to_ell(masks)
+    T = _tdtype(bf16)
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = to_dev(q, T), to_dev(k, T), to_dev(v, T)
+    dqp, dkp = to_dev(qperm, torch.int32), to_dev(kperm, torch.int32)
+    lists = (to_dev(qoff, torch.int32), to_dev(koff, torch.int32), to_dev(cnt, torch.int32),
+             to_dev(idx, torch.int32))
+    o_f, lse_f = sva_block_sparse_attn_perm(dq, dk, dv, dqp, dkp, *lists, scale, want_lse=True)
+    gq = torch.gather(dq, 2, dqp.long()[..., None].expand(-1, -1, -1, d))
+    gk = torch.gather(dk, 2, dkp.long()[..., None].expand(-1, -1, -1, d))
+    gv = torch.gather(dv, 2, dkp.long()[..., None].expand(-1, -1, -1, d))
+    o_p, lse_p = sva_block_sparse_attn(gq, gk, gv, *lists, scale, want_lse=True)
+    o_ref = torch.empty_like(o_p).scatter_(2, dqp.long()[..., None].expand(-1, -1, -1, d), o_p)
+    lse_ref = torch.empty_like(lse_p).scatter_(2, dqp.long(), lse_p)
+    assert torch.equal(o_f, o_ref)
+    assert torch.equal(lse_f, lse_ref)
+    o_f, lse_f = host(o_f), host(lse_f)
+    for h in range(heads):
+        # cluster id of each ORIGINAL row: permuted position -> block
+        aq = np.empty(nq, np.int64)
+        aq[qperm[0, h]] = np.repeat(np.arange(nqb), np.diff(qoff[0, h]))
+        ak = np.empty(nk, np.int64)
+        ak[kperm[0, h]] = np.repeat(np.arange(nkb), np.diff(koff[0, h]))
+        ro, rl = oracle.cluster_sparse_attention(q[0, h], k[0, h], v[0, h], aq, ak, masks[0, h],
+                                                 np.float32(scale))
+        check_attention(o_f[0, h], ro, bf16, f"head {h}")
+        check_lse(lse_f[0, h], rl, 1e-3 if bf16 else 1e-5)

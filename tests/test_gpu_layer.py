@@ -30,12 +30,14 @@ def _layer_inputs(cfg, heads=None):
     return x, iq, ik
 
 
-def test_tiny_end_to_end_fp32():
+@pytest.mark.parametrize("fused", [True, False])
+def test_tiny_end_to_end_fp32(fused):
     cfg = synth.CONFIGS["tiny"]
     x, iq, ik = _layer_inputs(cfg)
     dev = device()
     layer = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
-                                 cfg.top_p, dtype=torch.float32, device=dev, want_lse=True)
+                                 cfg.top_p, dtype=torch.float32, device=dev, want_lse=True,
+                                 fuse_permutation=fused)
     t = {k: to_dev(v) for k, v in x.items()}
     o = host(layer(t["q"], t["k"], t["v"], to_dev(iq), to_dev(ik)))
     for h in range(cfg.heads):
@@ -48,8 +50,11 @@ def test_tiny_end_to_end_fp32():
         assert np.array_equal(host(layer.off_k)[0, h], r["off_k"])
         assert np.array_equal(host(layer.mask)[0, h].astype(bool), r["select"].mask)
         check_attention(o[0, h], r["o"], False, f"head {h}")
-        lse = np.empty(cfg.n)                  # the layer's LSE is in permuted query order
-        lse[host(layer.perm_q)[0, h]] = host(layer.lse_p)[0, h]
+        if fused:                              # LSE in original token order
+            lse = host(layer.lse)[0, h]
+        else:                                  # LSE in permuted query order
+            lse = np.empty(cfg.n)
+            lse[host(layer.perm_q)[0, h]] = host(layer.lse)[0, h]
         assert np.abs(lse - r["lse"]).max() < 1e-5
 
 
@@ -134,14 +139,15 @@ def test_full_size_output_sampled(full_layer):
         check_attention(o[0, h, rows], ro, True, f"layer head {h}")
 
 
-def test_two_stream_forward_equals_sequential_stages():
+@pytest.mark.parametrize("fused", [True, False])
+def test_two_stream_forward_equals_sequential_stages(fused):
     # forward runs the Q clustering on a side stream, concurrently with K/V;
     # the result must be bit-identical to the stages run one after another
     cfg = synth.CONFIGS["5s"].with_(heads=4)
     x, iq, ik = _layer_inputs(cfg, heads=(0, 1, 2, 3))
     dev = device()
     layer = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
-                                 cfg.top_p, device=dev)
+                                 cfg.top_p, device=dev, fuse_permutation=fused)
     t = {k: to_dev(v, torch.bfloat16) for k, v in x.items()}
     iq_d, ik_d = to_dev(iq), to_dev(ik)
     outs = []
@@ -151,8 +157,30 @@ def test_two_stream_forward_equals_sequential_stages():
     layer.kmeans(t["q"], t["k"], iq_d, ik_d)
     layer.permute(t["q"], t["k"], t["v"])
     layer.select()
-    layer.attend()
+    layer.attend(t["q"], t["k"], t["v"])
     layer.unpermute()
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
     assert torch.equal(outs[0], layer.o)
+
+
+def test_fused_permutation_layer_equals_unfused():
+    # reading Q, K, V through the permutation inside attention (and writing O
+    # back in token order) gives the same bits as gather -> attend -> unpermute
+    cfg = synth.CONFIGS["5s"].with_(heads=3)
+    x, iq, ik = _layer_inputs(cfg, heads=(5, 6, 7))
+    dev = device()
+    t = {k: to_dev(v, torch.bfloat16) for k, v in x.items()}
+    iq_d, ik_d = to_dev(iq), to_dev(ik)
+    res = {}
+    for fused in (True, False):
+        layer = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
+                                     cfg.top_p, device=dev, want_lse=True,
+                                     fuse_permutation=fused)
+        layer(t["q"], t["k"], t["v"], iq_d, ik_d)
+        lse = layer.lse.clone()
+        if not fused:
+            lse = torch.empty_like(lse).scatter_(2, layer.perm_q.long(), lse)
+        res[fused] = (layer.o.clone(), lse, layer.perm_q.clone(), layer.mask.clone())
+    for a, b in zip(res[True], res[False]):
+        assert torch.equal(a, b)
