@@ -46,12 +46,15 @@ namespace sva {
 namespace {
 
 constexpr int kThreads = 256;       // helper kernels
-constexpr int kAttnThreads = 512;   // bf16 attention: 8 waves
-constexpr int kWaveRows = 32;       // query rows per wave (one 32-row MFMA tile)
-constexpr int kQTile = kWaveRows * (kAttnThreads / 64);   // query rows per workgroup (256)
+constexpr int kQTile = 256;        // query rows per work item (and per fp32 workgroup)
+// bf16 attention waves per workgroup; each wave owns kQTile / waves query rows
+// in 32-row MFMA tiles
+template <int D>
+constexpr int attn_waves() { return 8; }
 constexpr int kKT = 64;           // keys per chunk
-constexpr int kStages = 3;        // K/V chunk buffers in LDS (two chunks in flight)
+constexpr int kStages = 4;        // K/V chunk buffers in LDS (two in flight, two in use)
 constexpr int kLCap = 1024;       // kept-list entries staged in LDS at a time
+constexpr int kWin = 16;          // chunks per row-map window
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -340,8 +343,8 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention
 // ---------------------------------------------------------------------------
-template <int D, bool OUT_F32, bool PERM>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
+template <int D, bool OUT_F32, bool PERM, int W>
+__global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, void *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ q_perm, const int32_t *__restrict__ k_perm,
@@ -352,9 +355,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     int nkb, int dense, float scale_log2) {
   constexpr int PPR = D / 8;             // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;          // rows per 1 KB direct-to-LDS wave load
-  constexpr int LPW = PPR / (kAttnThreads / 64);   // such loads per wave per tensor per chunk
+  constexpr int kThr = 64 * W;
+  constexpr int LPW = PPR / W;           // such loads per wave per tensor per chunk
+  static_assert(LPW >= 1 && PPR % W == 0, "every wave copies whole 1 KB pieces");
   constexpr int NS = D / 16;             // k-steps of the S MFMA
   constexpr int ND = D / 32;             // d tiles of the O accumulator
+  constexpr int kWaveRows = kQTile / W;  // query rows per wave
   constexpr int NT = kWaveRows / 32;     // 32-query tiles per wave
   constexpr float kLazy = 8.f;           // rescale only when a row max grows by > 2^8
 
@@ -363,16 +369,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sV[kStages][kKT * D];
   __shared__ int32_t sStart[kLCap];
   __shared__ int32_t sCum[kLCap + 1];
-  __shared__ int32_t sRow[kStages][kKT];
+  __shared__ int32_t sWin[2][kWin * kKT];    // row-map windows (double-buffered)
   __shared__ int32_t sPerm[kStages][kKT];  // PERM: original row of each chunk key
-  __shared__ int32_t sFlag[kKT];          // row-map scratch, all zero between uses
-  __shared__ int32_t sWsum[kAttnThreads / 64];
+  __shared__ int32_t sWsum[W];
 
   __shared__ int32_t sNext;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  if (tid < kKT) sFlag[tid] = 0;          // ordered before first use by the setup barriers
 
   // one work item: rows [row0, row0 + 256) of Q block qb of slice bh
   auto item = [&](const int bh, const int qb, const int row0) {
@@ -411,6 +415,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
   }
 
   f32x16 oacc[NT][ND];
+  f32x16 sacc[NT][2];                  // scores of the chunk awaiting its softmax
+  bf16x8 pb[NT][4];                    // probabilities of the chunk awaiting its PV
+  const bool late = wave >= W / 2;     // runs the rotated step (see below)
   float m_run[NT], l_run[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -459,11 +466,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
     // the segment's kept clusters as key-row ranges, empty ones dropped:
     // sStart[j] = first row, sCum[j] = virtual index of that row (exclusive scan)
     const int segn = min(kLCap, kc - seg0);
-    static_assert(kLCap == 2 * kAttnThreads, "two list entries per thread");
-    int st_r[2], len_r[2], ci[2];
+    constexpr int EPT = kLCap / kThr;     // list entries per thread
+    static_assert(EPT * kThr == kLCap && EPT <= 4, "the scan covers 4 entries per thread");
+    int st_r[EPT], len_r[EPT], ci[EPT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = tid + u * kAttnThreads;
+    for (int u = 0; u < EPT; ++u) {
+      const int j = tid + u * kThr;
       st_r[u] = 0;
       len_r[u] = 0;
       if (j < segn) {
@@ -478,46 +486,51 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       sCum[j] = len_r[u] > 0 ? 1 : 0;
     }
     __syncthreads();
-    block_exclusive_scan<kAttnThreads>(sCum, segn, sWsum);
+    block_exclusive_scan<kThr>(sCum, segn, sWsum);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) ci[u] = sCum[tid + u * kAttnThreads];
+    for (int u = 0; u < EPT; ++u) ci[u] = sCum[tid + u * kThr];
     const int nseg = sCum[segn];
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < EPT; ++u)
       if (len_r[u] > 0) {
         sStart[ci[u]] = st_r[u];
         sCum[ci[u]] = len_r[u];
       }
     __syncthreads();
-    block_exclusive_scan<kAttnThreads>(sCum, nseg, sWsum);
+    block_exclusive_scan<kThr>(sCum, nseg, sWsum);
     const int L = sCum[nseg];
     const int nch = (L + kKT - 1) / kKT;
     if (nch == 0) continue;   // uniform: L is shared
 
-    // Row map of chunk c (wave 0; chunks are mapped in order 0, 1, 2, ...):
-    // jcur is the range holding the chunk's first key.  Ranges are non-empty,
-    // so only the next 64 range starts can fall in the chunk or at the start
-    // of the next one; lane i takes start jcur+1+i.  Each start inside the
-    // chunk marks its position, and a ballot of the marks gives every lane the
-    // number of range starts at or before its key, hence its range.
-    int jcur = 0;
+    // Row maps in windows of kWin chunks: the K row behind each virtual key
+    // of the window (-1 past the end).  All threads build a window at once, a
+    // branchless binary search over the range starts per key; windows w and
+    // w+1 are double-buffered, and window w+1 is built in the first step of
+    // window w.
+    static_assert((kWin * kKT) % kThr == 0 && kLCap <= 1024, "window build geometry");
+    auto build_win = [&](int w) {
+      int32_t *dst = sWin[w & 1];
+#pragma unroll
+      for (int u = 0; u < kWin * kKT / kThr; ++u) {
+        const int i = tid + u * kThr;
+        const int v = w * (kWin * kKT) + i;
+        int lo = 0;   // the last range starting at or before v: largest j < nseg, sCum[j] <= v
+#pragma unroll
+        for (int b = 512; b > 0; b >>= 1) {
+          const int j = lo + b;
+          const int cj = sCum[min(j, nseg)];
+          lo = (j < nseg && cj <= v) ? j : lo;
+        }
+        dst[i] = v < L ? sStart[lo] + (v - sCum[lo]) : -1;
+      }
+    };
+    // PERM: wave 0 copies the original rows of chunk c's keys into the chunk's
+    // stage (from row 0 past the end, so every step issues one copy)
     auto rowmap = [&](int c, auto st) {
-      int32_t *dst = sRow[decltype(st)::value];
-      if (wave == 0) {
-        const int c0 = c * kKT;
-        const int jb = jcur + 1 + lane;
-        const int p = (jb <= nseg ? sCum[jb] : INT_MAX - kKT) - c0;   // >= 1; sCum[nseg] = L
-        const bool mark = p < kKT;
-        if (mark) sFlag[p] = 1;
-        const uint64_t starts = __ballot(sFlag[lane] != 0);
-        if (mark) sFlag[p] = 0;
-        const int seg = jcur + __popcll(starts & ((2ull << lane) - 1));
-        const int vv = c0 + lane;
-        const int rr = vv < L ? sStart[seg] + (vv - sCum[seg]) : -1;
-        dst[lane] = rr;
-        jcur += __popcll(__ballot(p <= kKT));     // the range holding key c0 + 64
-        if constexpr (PERM) {   // original rows: copied HBM -> LDS like the K/V rows
+      if constexpr (PERM) {
+        if (wave == 0) {
+          const int rr = c * kKT < L ? sWin[(c / kWin) & 1][(c % kWin) * kKT + lane] : -1;
           const int32_t *src = pbase + (rr < 0 ? 0 : rr);
           __builtin_amdgcn_global_load_lds(
               src, (__attribute__((address_space(3))) void *)&sPerm[decltype(st)::value][0], 4, 0, 0);
@@ -525,13 +538,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       }
     };
     // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
-    auto issue_loads = [&](auto st) {
-      const int32_t *rows = sRow[decltype(st)::value];
+    auto issue_loads = [&](auto st, int cc) {
+      const bool live = cc * kKT < L;   // uniform
+      const int32_t *rows = sWin[(cc / kWin) & 1] + (cc % kWin) * kKT;
       uint16_t *dk = sK[decltype(st)::value];
       uint16_t *dv = sV[decltype(st)::value];
-      // past the end of the list (the two chunks after the last) whole stages are
+      // past the end of the list (the chunks after the last) whole stages are
       // refilled from key row 0, so every step issues the same number of copies
-      int dummy = max(rows[0], 0);
+      int dummy = live ? max(rows[0], 0) : 0;
       int prow[LPW];
       if constexpr (PERM) {   // original rows of this lane's keys (and of key 0)
         const uint32_t pb = lds_offset(&sPerm[decltype(st)::value][0]);
@@ -541,7 +555,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
         pa[LPW] = pb;
         int pv[LPW + 1];
         lds_read_i32s(pv, pa);
-        dummy = rows[0] < 0 ? 0 : pv[LPW];
+        dummy = live && rows[0] >= 0 ? pv[LPW] : 0;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) prow[j] = pv[j];
       }
@@ -549,7 +563,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       for (int j = 0; j < LPW; ++j) {
         const int blk = wave * LPW + j;
         const int r = RPI * blk + ld_rsub;
-        int phys = rows[r];
+        int phys = live ? rows[r] : -1;
         if constexpr (PERM) phys = phys < 0 ? -1 : prow[j];
         phys = phys < 0 ? dummy : phys;
         // (offsets stay in named variables: with an arithmetic expression in the
@@ -565,100 +579,119 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
       }
     };
 
-    // prologue: chunks 0 and 1 in flight, row map of chunk 2 ready (a row map
-    // past the end of the list is all -1)
+    // prologue: row-map windows 0 and 1, chunks 0 and 1 in flight (and, PERM,
+    // the original rows of chunk 2 on their way)
+    build_win(0);
+    if (kWin < nch) build_win(1);
+    __syncthreads();
     rowmap(0, std::integral_constant<int, 0>{});
     rowmap(1, std::integral_constant<int, 1>{});
     rowmap(2, std::integral_constant<int, 2>{});
     if constexpr (PERM) wait_vmcnt<1>();   // original rows of chunks 0, 1 landed (wave 0)
     lds_barrier();
-    issue_loads(std::integral_constant<int, 0>{});
-    issue_loads(std::integral_constant<int, 1>{});
+    issue_loads(std::integral_constant<int, 0>{}, 0);
+    issue_loads(std::integral_constant<int, 1>{}, 1);
 
-    // chunk c lives in stage c % 3; the body is instantiated per stage
-    auto step = [&](auto st, int c) {
-      constexpr int S = decltype(st)::value;
-      // chunk c has landed once only chunk c+1's copies are outstanding; after
-      // the barrier every wave's copies of chunk c are in LDS and every wave is
-      // done with chunk c-1, whose stage chunk c+2 then refills
-      // (PERM: wave 0's copy of the original rows of chunk c+2 is older than
-      // chunk c+1's K/V copies, so it has landed too)
-      wait_vmcnt<2 * LPW>();
-      lds_barrier();
-      rowmap(c + 3, std::integral_constant<int, S>{});
-      issue_loads(std::integral_constant<int, (S + 2) % 3>{});
-
-      if (wave_active) {
-        // S^T = K Q^T for 64 keys (two 32-key m-tiles) x the wave's query tiles;
-        // each K fragment is read once per chunk and used by every query tile
-        f32x16 sacc[NT][2];
+    // S^T = K Q^T for the 64 keys of the chunk in stage ST (two 32-key m-tiles)
+    // x the wave's query tiles; each K fragment serves every query tile
+    auto qk = [&](auto st) {
+      constexpr int ST = decltype(st)::value;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          bf16x8 kf[NS];
-          if (mt == 0) lds_read_frags<S * kStageBytes>(kf, ka);
-          else lds_read_frags<S * kStageBytes + 32 * D * 2>(kf, ka);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[nt][mt][i] = 0.f;
-            if (!nt_active[nt]) continue;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) sacc[nt][mt] = mfma32x32x16(kf[s], qf[nt][s], sacc[nt][mt]);
-          }
-        }
-        bf16x8 pb[NT][4];
+      for (int mt = 0; mt < 2; ++mt) {
+        bf16x8 kf[NS];
+        if (mt == 0) lds_read_frags<ST * kStageBytes>(kf, ka);
+        else lds_read_frags<ST * kStageBytes + 32 * D * 2>(kf, ka);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[nt][mt][i] = 0.f;
           if (!nt_active[nt]) continue;
-          if ((c + 1) * kKT > L) {     // partial last chunk: mask keys past the end
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+          for (int s = 0; s < NS; ++s) sacc[nt][mt] = mfma32x32x16(kf[s], qf[nt][s], sacc[nt][mt]);
+        }
+      }
+    };
+    // online softmax of chunk cc: scores in sacc -> bf16 probabilities in pb,
+    // running max / sum updated, O rescaled when the max grows by > 2^kLazy
+    auto softmax = [&](int cc) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i)
-                if (c * kKT + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
-          }
-          // (maximum, not maxnum: no NaN canonicalisation, so v_maximum3 does 2 per op)
-          float mx = -INFINITY;
+      for (int nt = 0; nt < NT; ++nt) {
+        if (!nt_active[nt]) continue;
+        if ((cc + 1) * kKT > L) {     // partial last chunk: mask keys past the end
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sacc[nt][mt][i]);
-          {   // both lane halves hold the same query: exchange with permlane32_swap
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                             __float_as_uint(mx), false, false);
-            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            for (int i = 0; i < 16; ++i)
+              if (cc * kKT + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
+        }
+        // (maximum, not maxnum: no NaN canonicalisation, so v_maximum3 does 2 per
+        // op); four independent chains keep the reduction short
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            m4[i & 3] = __builtin_elementwise_maximum(m4[i & 3], sacc[nt][mt][i]);
+        float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]),
+                                                 __builtin_elementwise_maximum(m4[2], m4[3]));
+        {   // both lane halves hold the same query: exchange with permlane32_swap
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                           __float_as_uint(mx), false, false);
+          mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mxs = mx * scale_log2;           // finite: the chunk has a key
+        if (__any(mxs > m_run[nt] + kLazy)) {
+          const float m_new = fmaxf(m_run[nt], mxs);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+          m_run[nt] = m_new;
+        }
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_run[nt]));
+            ps[i & 3] += p;
+            pb[nt][2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
           }
-          const float mxs = mx * scale_log2;           // finite: the chunk has a key
-          if (__any(mxs > m_run[nt] + kLazy)) {
-            const float m_new = fmaxf(m_run[nt], mxs);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-            l_run[nt] *= alpha;
+        l_run[nt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      }
+    };
+    // O^T += V^T P^T with the V rows in stage ST; the V operand (transposing
+    // reads of row-major V) is shared by all query tiles
+    auto pv = [&](auto st) {
+      constexpr int ST = decltype(st)::value;
+      if constexpr (ND == 4) {   // two k-steps per LDS round trip
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          bf16x8 vf[2][ND];
+          if (kp == 0)
+            lds_read_vt2<ST * kStageBytes, ST * kStageBytes + 16 * D * 2, 8 * D * 2>(vf[0], vf[1], va);
+          else
+            lds_read_vt2<ST * kStageBytes + 32 * D * 2, ST * kStageBytes + 48 * D * 2, 8 * D * 2>(
+                vf[0], vf[1], va);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
-            m_run[nt] = m_new;
-          }
-          float ps = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_run[nt]));
-              ps += p;
-              pb[nt][2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
-            }
-          l_run[nt] += ps;
+              for (int nt = 0; nt < NT; ++nt)
+                if (nt_active[nt])
+                  oacc[nt][dt] = mfma32x32x16(vf[u][dt], pb[nt][2 * kp + u], oacc[nt][dt]);
         }
-        // O^T += V^T P^T; the V operand (transposing reads of row-major V) is
-        // shared by all query tiles
+      } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           bf16x8 vf[ND];
-          if (ks == 0) lds_read_vt<S * kStageBytes, 8 * D * 2>(vf, va);
-          else if (ks == 1) lds_read_vt<S * kStageBytes + 16 * D * 2, 8 * D * 2>(vf, va);
-          else if (ks == 2) lds_read_vt<S * kStageBytes + 32 * D * 2, 8 * D * 2>(vf, va);
-          else lds_read_vt<S * kStageBytes + 48 * D * 2, 8 * D * 2>(vf, va);
+          if (ks == 0) lds_read_vt<ST * kStageBytes, 8 * D * 2>(vf, va);
+          else if (ks == 1) lds_read_vt<ST * kStageBytes + 16 * D * 2, 8 * D * 2>(vf, va);
+          else if (ks == 2) lds_read_vt<ST * kStageBytes + 32 * D * 2, 8 * D * 2>(vf, va);
+          else lds_read_vt<ST * kStageBytes + 48 * D * 2, 8 * D * 2>(vf, va);
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -667,10 +700,42 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(
         }
       }
     };
-    for (int c = 0; c < nch; c += 3) {
+
+    // Step c (c = 0 .. nch; chunk c lives in stage c % 4, the body is
+    // instantiated per stage).  The two waves sharing a SIMD (w, w + W/2) run
+    // the same sequence -- softmax, PV, QK -- rotated against each other:
+    //   waves 0 .. W/2-1:   PV(c-1), QK(c), softmax(c)
+    //   waves W/2 .. W-1:   softmax(c-1), PV(c-1), QK(c)
+    // so while one of them is in its MFMA phase the other is in its VALU
+    // phase.  Chunk c-1's V stays in use during step c, hence four stages
+    // for two chunks in flight.  Step nch only finishes chunk nch-1.
+    auto step = [&](auto st, int c) {
+      constexpr int S = decltype(st)::value;
+      constexpr int SP = (S + kStages - 1) % kStages;   // stage of chunk c-1
+      // chunk c has landed once only chunk c+1's copies are outstanding; after
+      // the barrier every wave's copies of chunk c are in LDS and every wave is
+      // done with chunk c-2, whose stage chunk c+2 then refills
+      // (PERM: wave 0's copy of the original rows of chunk c+2 is older than
+      // chunk c+1's K/V copies, so it has landed too)
+      wait_vmcnt<2 * LPW>();
+      lds_barrier();
+      if (c % kWin == 0 && (c / kWin + 1) * kWin < nch) build_win(c / kWin + 1);
+      rowmap(c + 3, std::integral_constant<int, (S + 3) % kStages>{});
+      issue_loads(std::integral_constant<int, (S + 2) % kStages>{}, c + 2);
+
+      if (wave_active) {
+        if (late && c > 0) softmax(c - 1);
+        if (c > 0) pv(std::integral_constant<int, SP>{});
+        if (c < nch) qk(std::integral_constant<int, S>{});
+        if (!late && c < nch) softmax(c);
+      }
+    };
+    static_assert(kStages == 4, "the step loop is unrolled over four stages");
+    for (int c = 0; c <= nch; c += 4) {
       step(std::integral_constant<int, 0>{}, c);
-      if (c + 1 < nch) step(std::integral_constant<int, 1>{}, c + 1);
-      if (c + 2 < nch) step(std::integral_constant<int, 2>{}, c + 2);
+      if (c + 1 <= nch) step(std::integral_constant<int, 1>{}, c + 1);
+      if (c + 2 <= nch) step(std::integral_constant<int, 2>{}, c + 2);
+      if (c + 3 <= nch) step(std::integral_constant<int, 3>{}, c + 3);
     }
     wait_vmcnt<0>();   // the copies past the end must land before the stages are reused
     lds_barrier();     // the next segment reuses the LDS buffers and lists
@@ -791,8 +856,9 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
 template <int D, bool OF>
 hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items,
                     const WorkItem *lists, int32_t *ctl, int grid, hipStream_t s) {
+  constexpr int kW = attn_waves<D>();
   if (a.q_perm != nullptr) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, OF, true>), dim3(grid), dim3(kAttnThreads), 0, s,
+    hipLaunchKernelGGL((attn_bf16_kernel<D, OF, true, kW>), dim3(grid), dim3(64 * kW), 0, s,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_perm, a.k_perm,
                        a.q_off, a.k_off, a.kept_count, a.kept_idx, a.kept_stride, work, cap,
@@ -800,7 +866,7 @@ hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_item
                        a.scale * kLog2e);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, OF, false>), dim3(grid), dim3(kAttnThreads), 0, s,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, OF, false, kW>), dim3(grid), dim3(64 * kW), 0, s,
                      static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                      static_cast<const uint16_t *>(a.v), a.o, a.lse, nullptr, nullptr, a.q_off,
                      a.k_off,

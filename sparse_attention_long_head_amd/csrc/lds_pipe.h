@@ -103,6 +103,44 @@ __device__ __forceinline__ void lds_read_vt(bf16x8 (&f)[N], const uint32_t (&a)[
   for (int i = 0; i < N; ++i) f[i] = __builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Two k-steps of transposed fragments at once (offsets OFF0 and OFF1, each
+// with rows +0 and +HI), for 4 d tiles: 16 reads, one wait.
+template <int OFF0, int OFF1, int HI>
+__device__ __forceinline__ void lds_read_vt2(bf16x8 (&f0)[4], bf16x8 (&f1)[4],
+                                             const uint32_t (&a)[4]) {
+  static_assert(OFF0 >= 0 && OFF1 + HI < 65536, "ds offset field");
+  bf16x4 l0[4], h0[4], l1[4], h1[4];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %6, %19 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %12, %18 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %13, %18 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l0[0]), "=&v"(h0[0]), "=&v"(l0[1]), "=&v"(h0[1]), "=&v"(l0[2]), "=&v"(h0[2]),
+        "=&v"(l0[3]), "=&v"(h0[3]), "=&v"(l1[0]), "=&v"(h1[0]), "=&v"(l1[1]), "=&v"(h1[1]),
+        "=&v"(l1[2]), "=&v"(h1[2]), "=&v"(l1[3]), "=&v"(h1[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF0), "i"(OFF0 + HI), "i"(OFF1),
+        "i"(OFF1 + HI)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f0[i] = __builtin_shufflevector(l0[i], h0[i], 0, 1, 2, 3, 4, 5, 6, 7);
+    f1[i] = __builtin_shufflevector(l1[i], h1[i], 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
 // Workgroup barrier for LDS only: this wave's LDS accesses complete, then
 // s_barrier.  Unlike __syncthreads() it does not wait for outstanding
 // global->LDS copies, which the K/V pipeline keeps in flight across it; the
@@ -128,10 +166,21 @@ __device__ __forceinline__ void lds_read_f32x4x4(f32x4 (&f)[4], uint32_t a) {
       : "memory");
 }
 
-// N ds_read_b32 (N = 2 or 3) at per-lane byte addresses a[i]; waits for them.
+// N ds_read_b32 (N = 2, 3 or 5) at per-lane byte addresses a[i]; waits for them.
 template <int N>
 __device__ __forceinline__ void lds_read_i32s(int (&v)[N], const uint32_t (&a)[N]) {
-  if constexpr (N == 3) {
+  if constexpr (N == 5) {
+    asm volatile(
+        "ds_read_b32 %0, %5\n\t"
+        "ds_read_b32 %1, %6\n\t"
+        "ds_read_b32 %2, %7\n\t"
+        "ds_read_b32 %3, %8\n\t"
+        "ds_read_b32 %4, %9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+        : "memory");
+  } else if constexpr (N == 3) {
     asm volatile(
         "ds_read_b32 %0, %3\n\t"
         "ds_read_b32 %1, %4\n\t"
@@ -141,7 +190,7 @@ __device__ __forceinline__ void lds_read_i32s(int (&v)[N], const uint32_t (&a)[N
         : "v"(a[0]), "v"(a[1]), "v"(a[2])
         : "memory");
   } else {
-    static_assert(N == 2, "2 or 3 reads");
+    static_assert(N == 2, "2, 3 or 5 reads");
     asm volatile(
         "ds_read_b32 %0, %2\n\t"
         "ds_read_b32 %1, %3\n\t"
