@@ -17,6 +17,9 @@ The method (Sparse VideoGen2 explainer, technical summary section 2,
   contiguous; the result is equivalent to dense attention.
 * ``select``      -- section 2.b: centroid-pair scores, then clusters are
   taken in descending score order until their cumulative sum reaches p.
+* ``radial``      -- DynamicRad explainer, technical summary section 2.a: the
+  radial candidate set, the static-ratio mask and block means (the proxies of
+  the dynamic-threshold mode, ``select.threshold_select``).
 * ``attention``   -- section 2.c (custom kernel) and section 1 (full 3-D
   attention): exact softmax attention restricted to the kept blocks, evaluated
   in original token coordinates (the oracle never permutes).
@@ -28,7 +31,10 @@ closed forms, and invariants.  No function here is "parity unpinned".
 """
 from .kmeans import assign_step, update_step, kmeans, objective, KMeansResult  # noqa: F401
 from .permute import cluster_permutation, permute_rows, unpermute_rows  # noqa: F401
-from .select import centroid_scores, top_p_select, SelectResult  # noqa: F401
+from .select import (centroid_scores, top_p_select, SelectResult,  # noqa: F401
+                     threshold_select, ThresholdResult)
+from .radial import (block_geometry, radial_candidates, static_ratio_mask,  # noqa: F401
+                     block_means)
 from .attention import (attend, full_attention, cluster_sparse_attention,  # noqa: F401
                         block_sparse_attention)
 from .pipeline import svg2_layer  # noqa: F401

@@ -22,6 +22,17 @@ Readings where the pages are silent:
   crosses p is kept); p >= 1 keeps every non-empty K cluster.  Because p > 0 and
   at least one K cluster is non-empty, a non-empty Q cluster always keeps one;
 * an empty Q cluster keeps nothing (it has no rows).
+
+``threshold_select`` is DynamicRad's dynamic-threshold ("quality-first") mode
+(DynamicRad explainer, technical summary section 2.a): pre-softmax logits serve
+as cheap importance proxies, one global threshold keeps only the high-scoring
+pairs, and a block left empty keeps its top-scoring pair so it never loses all
+context.  Readings: the proxy of block pair (i, j) is the centroid score S_ij
+above (block means on uniform blocks, cluster centroids after k-means); the
+threshold is absolute, S_ij >= theta; only pairs inside the candidate set (all
+pairs when none is given) whose key block is non-empty are eligible; a
+non-empty query block with no eligible pair at or above theta keeps its
+eligible argmax (ties by the lower key id); an empty query block keeps nothing.
 """
 from __future__ import annotations
 
@@ -85,3 +96,47 @@ def top_p_select(scores: np.ndarray, size_q: np.ndarray, size_k: np.ndarray,
         ids = np.flatnonzero(mask[i])
         kept_idx[i, :ids.size] = ids
     return SelectResult(mask, kept_count, kept_idx, weights, margin)
+
+
+@dataclass
+class ThresholdResult:
+    mask: np.ndarray        # bool [nq, nk]
+    kept_count: np.ndarray  # int64 [nq]
+    kept_idx: np.ndarray    # int64 [nq, nk]; ascending key ids, then -1
+    margin: np.ndarray      # float64 [nq]; distance of the row's decisions from a tie
+
+
+def threshold_select(scores: np.ndarray, size_q: np.ndarray, size_k: np.ndarray, theta: float,
+                     cand: np.ndarray = None) -> ThresholdResult:
+    scores = np.asarray(scores, np.float64)
+    nq, nk = scores.shape
+    size_q = np.asarray(size_q)
+    size_k = np.asarray(size_k)
+    elig = np.broadcast_to(size_k > 0, (nq, nk)).copy()
+    if cand is not None:
+        elig &= np.asarray(cand, dtype=bool)
+    mask = np.zeros((nq, nk), dtype=bool)
+    margin = np.full(nq, np.inf)
+    for i in range(nq):
+        if size_q[i] == 0:
+            continue
+        ids = np.flatnonzero(elig[i])
+        if ids.size == 0:
+            continue
+        s = scores[i, ids]
+        keep = s >= theta
+        margin[i] = float(np.min(np.abs(s - theta)))
+        if keep.any():
+            mask[i, ids[keep]] = True
+        else:   # the safeguard: the top-scoring eligible pair (lowest id on ties)
+            top = int(np.argmax(s))
+            mask[i, ids[top]] = True
+            rest = np.delete(s, top)
+            if rest.size:
+                margin[i] = min(margin[i], float(s[top] - rest.max()))
+    kept_count = mask.sum(axis=1).astype(np.int64)
+    kept_idx = np.full((nq, nk), -1, dtype=np.int64)
+    for i in range(nq):
+        ids = np.flatnonzero(mask[i])
+        kept_idx[i, :ids.size] = ids
+    return ThresholdResult(mask, kept_count, kept_idx, margin)
