@@ -11,10 +11,13 @@
  *   sva_block_sparse_attn attention over the kept blocks only       (section 2.c)
  *   sva_unpermute         inverse permutation of the output         (section 2.a)
  * plus the dense baseline sva_full_attn (full 3-D attention, the "VRAM wall" of
- * the long-video blog, atlascloud.ai, "Why long video is hard").  A fixed mask
- * over uniform token blocks (DynamicRad explainer, arXiv 2604.20470, technical
- * summary section 2.a, static-ratio mode) runs through sva_block_sparse_attn
- * with uniform offsets.
+ * the long-video blog, atlascloud.ai, "Why long video is hard").  DynamicRad's
+ * two selection modes (DynamicRad explainer, arXiv 2604.20470, technical
+ * summary section 2.a) work on uniform token blocks and feed the same
+ * attention with uniform offsets:
+ *   sva_radial_mask       radial candidate set + static ratio per temporal distance
+ *   sva_block_means       block means, the proxies of the dynamic mode
+ *   sva_select_threshold  global threshold on proxy logits, top pair kept if empty
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -137,6 +140,74 @@ int32_t sva_select_blocks(const float *cent_q, const int32_t *size_q, int32_t cq
                           int32_t heads, int32_t d, double scale, double top_p, uint8_t *mask,
                           int32_t *kept_count, int32_t *kept_idx, void *ws, size_t ws_bytes,
                           void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_select_threshold -- DynamicRad's dynamic-threshold ("quality-first")
+ * mode (DynamicRad explainer, technical summary section 2.a): pre-softmax
+ * logits as importance proxies, one global threshold, and a block that ends
+ * empty keeps its top-scoring pair.  For each (b,h) and each query block i
+ * with size_q[i] > 0, in fp64:
+ *   S_ij = (cent_q_i . cent_k_j) * scale    (the same arithmetic as
+ *                                            sva_select_blocks)
+ *   eligible: size_k[j] > 0 and (cand == NULL or cand[i][j] != 0)
+ *   keep every eligible j with S_ij >= theta; if none, keep the eligible j of
+ *   largest S_ij (ties: lowest j); if nothing is eligible, keep nothing.
+ * Query blocks with size_q[i] == 0 keep nothing.
+ *
+ *   cent_q [bh][nq][d] fp32, size_q [bh][nq] int32 (block means and sizes
+ *              from sva_block_means, or k-means centroids and sizes)
+ *   cent_k [bh][nk][d] fp32, size_k [bh][nk] int32
+ *   nq <= 65535, nk <= 4096; scale finite; theta any non-NaN value
+ *   cand       [nq][nk] uint8, DEVICE, shared by every slice, or NULL (all
+ *              pairs are candidates), e.g. a radial set from sva_radial_mask
+ *   mask, kept_count, kept_idx  OUT as in sva_select_blocks
+ * ------------------------------------------------------------------------ */
+int32_t sva_select_threshold(const float *cent_q, const int32_t *size_q, int32_t nq,
+                             const float *cent_k, const int32_t *size_k, int32_t nk,
+                             int32_t batch, int32_t heads, int32_t d, double scale, double theta,
+                             const uint8_t *cand, uint8_t *mask, int32_t *kept_count,
+                             int32_t *kept_idx, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_radial_mask -- DynamicRad's radial locality candidate set with its
+ * static-ratio ("throughput-first") selection (DynamicRad explainer,
+ * technical summary section 2.a: attention fades with spatial and temporal
+ * distance; the static mode keeps a fixed share of the candidates chosen by
+ * temporal distance, with no content scoring).  The mask depends on geometry
+ * only, so every slice gets the same one.
+ *
+ * Uniform blocks of `block` consecutive tokens (the last may be short),
+ * nb = ceil(n / block); token order is frame-major with hw tokens per frame.
+ * Block b lies in frame t_b = (block*b) / hw at window s_b = ((block*b) % hw)
+ * / block.  Candidates: dt = |t_a - t_b| <= dt_max and |s_a - s_b| <=
+ * window0 >> dt.  For query block a and each dt, of the n candidates at that
+ * distance the first ceil(ratios[dt] * n) in (|s_a - s_b|, b) order are kept
+ * (ceil evaluated in fp64 on the float ratio).  ratios of 1 keep the whole
+ * candidate set.
+ *
+ *   n, hw, block  >= 1;  0 <= dt_max <= 15;  window0 >= 0
+ *   ratios     HOST float[dt_max + 1], each in [0, 1]
+ *   mask       [bh][nb][nb] uint8 OUT
+ *   kept_count [bh][nb] int32 OUT
+ *   kept_idx   [bh][nb][nb] int32 OUT: kept key blocks ascending, then -1
+ *              (pass kept_stride = nb and uniform offsets to the attention)
+ * Rejected with SVA_EUNSUPPORTED when the 2*dt_max+1 frames around a block
+ * hold more than 8192 blocks.
+ * ------------------------------------------------------------------------ */
+int32_t sva_radial_mask(int32_t n, int32_t hw, int32_t block, int32_t dt_max, int32_t window0,
+                        const float *ratios, int32_t batch, int32_t heads, uint8_t *mask,
+                        int32_t *kept_count, int32_t *kept_idx, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * sva_block_means -- the mean of every uniform block of rows, the proxy of a
+ * block for sva_select_threshold (DynamicRad explainer, section 2.a).
+ *   x      [bh][n][d] of dtype; block >= 1; nb = ceil(n / block)
+ *   means  [bh][nb][d] fp32 OUT: rows summed in fp64 in row order, divided by
+ *          the row count, rounded to fp32
+ *   sizes  [bh][nb] int32 OUT: rows per block (block, the last may be short)
+ * ------------------------------------------------------------------------ */
+int32_t sva_block_means(const void *x, int32_t dtype, int32_t batch, int32_t heads, int32_t n,
+                        int32_t d, int32_t block, float *means, int32_t *sizes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * sva_block_sparse_attn -- attention over the kept blocks only (Sparse

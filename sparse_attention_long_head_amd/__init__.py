@@ -8,6 +8,7 @@ call does, and raises if it has not been built.
 from ._lib import (  # noqa: F401
     SVA_BF16, SVA_F32, LIB_PATH, lib, last_error,
     sva_kmeans, sva_permute, sva_select_blocks, sva_block_sparse_attn,
-    sva_block_sparse_attn_perm, sva_unpermute, sva_full_attn,
+    sva_block_sparse_attn_perm, sva_unpermute, sva_full_attn, sva_select_threshold,
+    sva_radial_mask, sva_block_means,
 )
-from .layer import SparseVideoAttention  # noqa: F401
+from .layer import RadialSparseAttention, SparseVideoAttention  # noqa: F401

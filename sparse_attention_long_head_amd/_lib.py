@@ -37,6 +37,10 @@ SIGNATURES = {
     "sva_select_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "sva_select_blocks": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _D, _D, _P, _P, _P, _P, _Z,
                                _P]),
+    "sva_select_threshold": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _D, _D, _P, _P, _P, _P,
+                                  _P]),
+    "sva_radial_mask": (_I, [_I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P]),
+    "sva_block_means": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "sva_attn_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "sva_block_sparse_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P,
                                    _I, _F, _P, _I, _P, _P, _Z, _P]),
@@ -171,6 +175,69 @@ def sva_select_blocks(cent_q: torch.Tensor, size_q: torch.Tensor, cent_k: torch.
                                    _ptr(kept_count), _ptr(kept_idx), None, 0, _stream(cent_q)),
            "sva_select_blocks")
     return mask, kept_count, kept_idx
+
+
+def sva_select_threshold(cent_q: torch.Tensor, size_q: torch.Tensor, cent_k: torch.Tensor,
+                         size_k: torch.Tensor, scale: float, theta: float,
+                         cand: Optional[torch.Tensor] = None,
+                         mask: Optional[torch.Tensor] = None,
+                         kept_count: Optional[torch.Tensor] = None,
+                         kept_idx: Optional[torch.Tensor] = None):
+    """Global threshold on proxy logits (top pair kept if a row ends empty).
+    Returns (mask u8, kept_count, kept_idx)."""
+    b, h, nq, d = cent_q.shape
+    nk = cent_k.shape[2]
+    dev = cent_q.device
+    if cand is not None and tuple(cand.shape) != (nq, nk):
+        raise ValueError(f"cand must be [{nq}, {nk}] uint8")
+    if mask is None:
+        mask = torch.empty((b, h, nq, nk), dtype=torch.uint8, device=dev)
+    if kept_count is None:
+        kept_count = torch.empty((b, h, nq), dtype=torch.int32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((b, h, nq, nk), dtype=torch.int32, device=dev)
+    _check(lib().sva_select_threshold(_ptr(cent_q), _ptr(size_q), nq, _ptr(cent_k), _ptr(size_k),
+                                      nk, b, h, d, float(scale), float(theta), _ptr(cand),
+                                      _ptr(mask), _ptr(kept_count), _ptr(kept_idx),
+                                      _stream(cent_q)), "sva_select_threshold")
+    return mask, kept_count, kept_idx
+
+
+def sva_radial_mask(n: int, hw: int, block: int, dt_max: int, window0: int, ratios,
+                    batch: int, heads: int, device, mask: Optional[torch.Tensor] = None,
+                    kept_count: Optional[torch.Tensor] = None,
+                    kept_idx: Optional[torch.Tensor] = None):
+    """Radial candidate set with a static ratio per temporal distance (uniform
+    blocks).  Returns (mask u8 [b,h,nb,nb], kept_count, kept_idx)."""
+    nb = -(-n // block)
+    dev = torch.device(device)
+    if len(ratios) != dt_max + 1:
+        raise ValueError("one ratio per temporal distance 0..dt_max")
+    r = (ctypes.c_float * (dt_max + 1))(*[float(x) for x in ratios])
+    if mask is None:
+        mask = torch.empty((batch, heads, nb, nb), dtype=torch.uint8, device=dev)
+    if kept_count is None:
+        kept_count = torch.empty((batch, heads, nb), dtype=torch.int32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((batch, heads, nb, nb), dtype=torch.int32, device=dev)
+    _check(lib().sva_radial_mask(n, hw, block, dt_max, window0, ctypes.cast(r, _P), batch, heads,
+                                 _ptr(mask), _ptr(kept_count), _ptr(kept_idx), _stream(mask)),
+           "sva_radial_mask")
+    return mask, kept_count, kept_idx
+
+
+def sva_block_means(x: torch.Tensor, block: int, means: Optional[torch.Tensor] = None,
+                    sizes: Optional[torch.Tensor] = None):
+    """Mean of every uniform block of rows.  Returns (means fp32 [b,h,nb,d], sizes int32)."""
+    b, h, n, d = x.shape
+    nb = -(-n // block)
+    if means is None:
+        means = torch.empty((b, h, nb, d), dtype=torch.float32, device=x.device)
+    if sizes is None:
+        sizes = torch.empty((b, h, nb), dtype=torch.int32, device=x.device)
+    _check(lib().sva_block_means(_ptr(x), _dtype_code(x), b, h, n, d, block, _ptr(means),
+                                 _ptr(sizes), _stream(x)), "sva_block_means")
+    return means, sizes
 
 
 def sva_block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

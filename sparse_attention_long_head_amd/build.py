@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsva.so")
-SOURCES = ["sva_api.hip", "attention.hip", "kmeans.hip", "permute.hip", "select.hip"]
+SOURCES = ["sva_api.hip", "attention.hip", "kmeans.hip", "permute.hip", "select.hip", "radial.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -1,0 +1,137 @@
+// DynamicRad's radial candidate set and static-ratio mask, and block means
+// (the proxies of its dynamic-threshold mode), for gfx950.  DynamicRad
+// explainer, technical summary section 2.a: one radial locality candidate set
+// (block attention fades with spatial and temporal distance) and two modes;
+// the static-ratio mode keeps a fixed share of the candidates per temporal
+// distance with no content scoring.
+//
+// Uniform blocks of `block` consecutive tokens on the frame-major token grid:
+// block b starts at token block*b, lies in frame t_b = (block*b) / hw and at
+// window index s_b = ((block*b) % hw) / block.  (a, b) is a candidate when
+// dt = |t_a - t_b| <= dt_max and |s_a - s_b| <= window0 >> dt.  The static
+// ratio keeps, for each query block and each dt, the first ceil(r[dt] * n)
+// of the n candidates at that distance in (|s_a - s_b|, b) order.
+#include <math.h>
+
+#include "../../include/sva.h"
+#include "sva_internal.h"
+
+namespace sva {
+namespace {
+
+constexpr int kRadThreads = 256;
+
+__device__ __forceinline__ long long first_block(long long frame, int hw, int block) {
+  return (frame * hw + block - 1) / block;   // first block starting in the frame
+}
+
+// One workgroup per query block: wave 0 walks the blocks of frames
+// t_a - dt_max .. t_a + dt_max (the only ones that can be candidates) and
+// builds the ascending kept list; then every thread writes the row for every
+// slice (the mask does not depend on content, so all slices share it).
+__global__ __launch_bounds__(kRadThreads) void radial_kernel(RadialParams p, int bh,
+                                                             uint8_t *__restrict__ mask,
+                                                             int32_t *__restrict__ kept_count,
+                                                             int32_t *__restrict__ kept_idx) {
+  __shared__ int32_t sKept[kMaxRadialRow];
+  __shared__ int32_t sCnt;
+  const int a = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const long long start_a = static_cast<long long>(a) * p.block;
+  const int ta = static_cast<int>(start_a / p.hw);
+  const int sa = static_cast<int>((start_a % p.hw) / p.block);
+  const long long b_lo = first_block(max(0, ta - p.dt_max), p.hw, p.block);
+  const long long b_hi = min(static_cast<long long>(p.nb),
+                             first_block(static_cast<long long>(ta) + p.dt_max + 1, p.hw, p.block));
+  if (tid < 64) {
+    int cnt = 0;
+    for (long long base = b_lo; base < b_hi; base += 64) {
+      const long long b = base + lane;
+      bool keep = false;
+      if (b < b_hi) {
+        const long long sb0 = b * p.block;
+        const int tb = static_cast<int>(sb0 / p.hw);
+        const int sb = static_cast<int>((sb0 % p.hw) / p.block);
+        const int dt = abs(ta - tb), ds = abs(sa - sb);
+        if (dt <= p.dt_max && ds <= (p.window0 >> dt)) {
+          // rank of b among the candidates at distance dt, and their number
+          int n = 0, rank = 0;
+          for (int side = 0; side < (dt == 0 ? 1 : 2); ++side) {
+            const int f = side == 0 ? ta - dt : ta + dt;
+            if (f < 0) continue;
+            const long long f_lo = first_block(f, p.hw, p.block);
+            const long long f_hi = min(static_cast<long long>(p.nb), first_block(f + 1LL, p.hw, p.block));
+            for (long long b2 = f_lo; b2 < f_hi; ++b2) {
+              const int s2 = static_cast<int>(((b2 * p.block) % p.hw) / p.block);
+              const int ds2 = abs(sa - s2);
+              if (ds2 <= (p.window0 >> dt)) {
+                ++n;
+                if (ds2 < ds || (ds2 == ds && b2 < b)) ++rank;
+              }
+            }
+          }
+          const int k = static_cast<int>(ceil(static_cast<double>(p.ratio[dt]) * n));
+          keep = rank < k;
+        }
+      }
+      const uint64_t bal = __ballot(keep);
+      if (keep) sKept[cnt + __popcll(bal & ((1ull << lane) - 1))] = static_cast<int32_t>(b);
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) sCnt = cnt;
+  }
+  __syncthreads();
+  const int cnt = sCnt;
+  for (int s = 0; s < bh; ++s) {
+    const size_t row = static_cast<size_t>(s) * p.nb + a;
+    uint8_t *mrow = mask + row * p.nb;
+    int32_t *irow = kept_idx + row * p.nb;
+    for (int j = tid; j < p.nb; j += kRadThreads) {
+      mrow[j] = 0;
+      irow[j] = j < cnt ? sKept[j] : -1;
+    }
+    __syncthreads();   // the zeros land before the kept flags of this row
+    for (int j = tid; j < cnt; j += kRadThreads) mrow[sKept[j]] = 1;
+    if (tid == 0) kept_count[row] = cnt;
+  }
+}
+
+// One workgroup per (block, slice), one thread per column: the block's rows
+// summed in fp64 in row order, divided by the row count, stored as fp32.
+template <typename T>
+__global__ void block_means_kernel(const T *__restrict__ x, int n, int d, int block, int nb,
+                                   float *__restrict__ means, int32_t *__restrict__ sizes) {
+  const int b = blockIdx.x, s = blockIdx.y, col = threadIdx.x;
+  const int r0 = b * block, r1 = min(n, r0 + block);
+  const T *base = x + (static_cast<size_t>(s) * n + r0) * d + col;
+  double acc = 0.0;
+  for (int r = r0; r < r1; ++r, base += d) {
+    if constexpr (sizeof(T) == 2) acc += static_cast<double>(bf16_bits_to_f32(*base));
+    else acc += static_cast<double>(*base);
+  }
+  means[(static_cast<size_t>(s) * nb + b) * d + col] = static_cast<float>(acc / (r1 - r0));
+  if (col == 0) sizes[static_cast<size_t>(s) * nb + b] = r1 - r0;
+}
+
+}  // namespace
+
+hipError_t launch_radial_mask(const RadialParams &p, int32_t bh, uint8_t *mask,
+                              int32_t *kept_count, int32_t *kept_idx, hipStream_t s) {
+  hipLaunchKernelGGL(radial_kernel, dim3(p.nb), dim3(kRadThreads), 0, s, p, bh, mask, kept_count,
+                     kept_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_means(const void *x, int32_t dtype, int32_t bh, int32_t n, int32_t d,
+                              int32_t block, float *means, int32_t *sizes, hipStream_t s) {
+  const int nb = (n + block - 1) / block;
+  const dim3 grid(nb, bh);
+  if (dtype == SVA_BF16)
+    hipLaunchKernelGGL(block_means_kernel<uint16_t>, grid, dim3(d), 0, s,
+                       static_cast<const uint16_t *>(x), n, d, block, nb, means, sizes);
+  else
+    hipLaunchKernelGGL(block_means_kernel<float>, grid, dim3(d), 0, s,
+                       static_cast<const float *>(x), n, d, block, nb, means, sizes);
+  return hipGetLastError();
+}
+
+}  // namespace sva

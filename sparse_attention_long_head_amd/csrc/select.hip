@@ -211,7 +211,122 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   if (tid == 0) kept_count[static_cast<size_t>(bh) * cq + i] = m;
 }
 
+// DynamicRad's dynamic-threshold mode: one workgroup per (slice, query
+// block), fp64 proxies S_j = (mu_q . mu_k_j) * scale computed exactly as in
+// the top-p kernel; eligible pairs (non-empty key block, inside the candidate
+// set) with S_j >= theta are kept; a non-empty query block left with none keeps
+// its eligible argmax (ties: lower j).
+template <int D>
+__global__ __launch_bounds__(kThreads) void threshold_kernel(
+    const float *__restrict__ cent_q, const int32_t *__restrict__ size_q,
+    const float *__restrict__ cent_k, const int32_t *__restrict__ size_k, int nq, int nk,
+    double scale, double theta, const uint8_t *__restrict__ cand, uint8_t *__restrict__ mask,
+    int32_t *__restrict__ kept_count, int32_t *__restrict__ kept_idx) {
+  __shared__ uint8_t mk[kCap];
+  __shared__ double sq[D];
+  __shared__ double red[kThreads / 64];
+  __shared__ int ired[kThreads / 64];
+
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  uint8_t *mrow = mask + (static_cast<size_t>(bh) * nq + i) * nk;
+  int32_t *irow = kept_idx + (static_cast<size_t>(bh) * nq + i) * nk;
+  const int32_t *szk = size_k + static_cast<size_t>(bh) * nk;
+  if (size_q[static_cast<size_t>(bh) * nq + i] == 0) {
+    for (int j = tid; j < nk; j += kThreads) {
+      mrow[j] = 0;
+      irow[j] = -1;
+    }
+    if (tid == 0) kept_count[static_cast<size_t>(bh) * nq + i] = 0;
+    return;
+  }
+  if (tid < D) sq[tid] = static_cast<double>(cent_q[(static_cast<size_t>(bh) * nq + i) * D + tid]);
+  __syncthreads();
+
+  int lkept = 0;
+  double best = -INFINITY;
+  int best_j = 0x7fffffff;
+  for (int j = tid; j < nk; j += kThreads) {
+    const float *kr = cent_k + (static_cast<size_t>(bh) * nk + j) * D;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s = fma(sq[d], static_cast<double>(kr[d]), s);
+    s *= scale;
+    const bool elig = szk[j] > 0 && (cand == nullptr || cand[static_cast<size_t>(i) * nk + j] != 0);
+    const bool keep = elig && s >= theta;
+    mk[j] = keep ? 1 : 0;
+    lkept += keep ? 1 : 0;
+    if (elig && (best_j == 0x7fffffff || s > best || (s == best && j < best_j))) {
+      best = s;
+      best_j = j;
+    }
+  }
+  int total = block_reduce_isum(lkept, ired);
+  if (total == 0) {   // the safeguard: argmax over eligible pairs, lower id on ties
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(best, o);
+      const int oj = __shfl_xor(best_j, o);
+      if (oj != 0x7fffffff && (best_j == 0x7fffffff || ob > best || (ob == best && oj < best_j))) {
+        best = ob;
+        best_j = oj;
+      }
+    }
+    if (lane == 0) {
+      red[wave] = best;
+      ired[wave] = best_j;
+    }
+    __syncthreads();
+    double b = red[0];
+    int bj = ired[0];
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (ired[w] != 0x7fffffff && (bj == 0x7fffffff || red[w] > b || (red[w] == b && ired[w] < bj))) {
+        b = red[w];
+        bj = ired[w];
+      }
+    __syncthreads();
+    if (bj != 0x7fffffff) {
+      if (tid == 0) mk[bj] = 1;
+      total = 1;
+    }
+  }
+  __syncthreads();
+  // ascending compaction of the kept ids
+  const int cper = (nk + kThreads - 1) / kThreads;
+  const int c0 = min(nk, tid * cper), c1 = min(nk, c0 + cper);
+  int cnt = 0;
+  for (int j = c0; j < c1; ++j) cnt += mk[j];
+  int xi = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(xi, o);
+    if (lane >= o) xi += y;
+  }
+  if (lane == 63) ired[wave] = xi;
+  __syncthreads();
+  int pos = xi - cnt;
+  for (int w = 0; w < wave; ++w) pos += ired[w];
+  for (int j = c0; j < c1; ++j) {
+    mrow[j] = mk[j];
+    if (mk[j]) irow[pos++] = j;
+  }
+  for (int j = total + tid; j < nk; j += kThreads) irow[j] = -1;
+  if (tid == 0) kept_count[static_cast<size_t>(bh) * nq + i] = total;
+}
+
 }  // namespace
+
+hipError_t launch_select_threshold(const ThresholdArgs &a, hipStream_t s) {
+  const dim3 grid(a.nq, a.bh);
+  if (a.d == 128)
+    hipLaunchKernelGGL(threshold_kernel<128>, grid, dim3(kThreads), 0, s, a.cent_q, a.size_q,
+                       a.cent_k, a.size_k, a.nq, a.nk, a.scale, a.theta, a.cand, a.mask,
+                       a.kept_count, a.kept_idx);
+  else
+    hipLaunchKernelGGL(threshold_kernel<64>, grid, dim3(kThreads), 0, s, a.cent_q, a.size_q,
+                       a.cent_k, a.size_k, a.nq, a.nk, a.scale, a.theta, a.cand, a.mask,
+                       a.kept_count, a.kept_idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   int ckp = 1;

@@ -157,6 +157,72 @@ int32_t sva_select_blocks(const float *cent_q, const int32_t *size_q, int32_t cq
   return hip_status(sva::launch_select(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int32_t sva_select_threshold(const float *cent_q, const int32_t *size_q, int32_t nq,
+                             const float *cent_k, const int32_t *size_k, int32_t nk,
+                             int32_t batch, int32_t heads, int32_t d, double scale, double theta,
+                             const uint8_t *cand, uint8_t *mask, int32_t *kept_count,
+                             int32_t *kept_idx, void *stream) {
+  const char *fn = "sva_select_threshold";
+  if (!cent_q || !size_q || !cent_k || !size_k || !mask || !kept_count || !kept_idx)
+    return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_slices(fn, batch, heads, 1));
+  SVA_TRY(check_d(fn, d));
+  if (nq < 1 || nk < 1) return fail(SVA_EINVAL, "%s: nq and nk must be >= 1", fn);
+  if (nq > 65535) return fail(SVA_EUNSUPPORTED, "%s: nq=%d exceeds 65535", fn, nq);
+  if (nk > sva::kMaxSelectK)
+    return fail(SVA_EUNSUPPORTED, "%s: nk=%d exceeds %d", fn, nk, sva::kMaxSelectK);
+  if (!isfinite(scale)) return fail(SVA_EINVAL, "%s: scale must be finite", fn);
+  if (isnan(theta)) return fail(SVA_EINVAL, "%s: theta is NaN", fn);
+  sva::ThresholdArgs a{cent_q, cent_k, size_q, size_k, batch * heads, nq, nk, d, scale, theta,
+                       cand, mask, kept_count, kept_idx};
+  return hip_status(sva::launch_select_threshold(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t sva_radial_mask(int32_t n, int32_t hw, int32_t block, int32_t dt_max, int32_t window0,
+                        const float *ratios, int32_t batch, int32_t heads, uint8_t *mask,
+                        int32_t *kept_count, int32_t *kept_idx, void *stream) {
+  const char *fn = "sva_radial_mask";
+  if (!ratios || !mask || !kept_count || !kept_idx)
+    return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_slices(fn, batch, heads, n));
+  if (hw < 1 || block < 1) return fail(SVA_EINVAL, "%s: hw and block must be >= 1", fn);
+  if (dt_max < 0 || dt_max > sva::kMaxRadialDt)
+    return fail(SVA_EINVAL, "%s: dt_max must be in [0, %d] (got %d)", fn, sva::kMaxRadialDt, dt_max);
+  if (window0 < 0) return fail(SVA_EINVAL, "%s: window0 must be >= 0", fn);
+  sva::RadialParams p{};
+  p.n = n;
+  p.hw = hw;
+  p.block = block;
+  p.nb = static_cast<int32_t>((static_cast<long long>(n) + block - 1) / block);
+  p.dt_max = dt_max;
+  p.window0 = window0;
+  for (int t = 0; t <= dt_max; ++t) {
+    if (!(ratios[t] >= 0.f && ratios[t] <= 1.f))
+      return fail(SVA_EINVAL, "%s: ratios[%d] must be in [0, 1] (got %g)", fn, t, ratios[t]);
+    p.ratio[t] = ratios[t];
+  }
+  const long long span = (2LL * dt_max + 1) * (hw / block + 2) + 1;
+  if (span > sva::kMaxRadialRow)
+    return fail(SVA_EUNSUPPORTED, "%s: %lld candidate blocks per row exceed %d", fn, span,
+                sva::kMaxRadialRow);
+  if (static_cast<long long>(batch) * heads * p.nb * p.nb > (1LL << 40))
+    return fail(SVA_EUNSUPPORTED, "%s: mask too large", fn);
+  return hip_status(sva::launch_radial_mask(p, batch * heads, mask, kept_count, kept_idx,
+                                            static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t sva_block_means(const void *x, int32_t dtype, int32_t batch, int32_t heads, int32_t n,
+                        int32_t d, int32_t block, float *means, int32_t *sizes, void *stream) {
+  const char *fn = "sva_block_means";
+  if (!x || !means || !sizes) return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
+  SVA_TRY(check_slices(fn, batch, heads, n));
+  SVA_TRY(check_d(fn, d));
+  if (block < 1) return fail(SVA_EINVAL, "%s: block must be >= 1", fn);
+  return hip_status(sva::launch_block_means(x, dtype, batch * heads, n, d, block, means, sizes,
+                                            static_cast<hipStream_t>(stream)), fn);
+}
+
 // ---------------------------------------------------------------------------
 static int32_t check_attn(const char *fn, const void *q, const void *k, const void *v,
                           int32_t dtype, int32_t batch, int32_t heads, int32_t n_q, int32_t n_k,

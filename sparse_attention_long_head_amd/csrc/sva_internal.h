@@ -94,6 +94,28 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 
+struct ThresholdArgs {
+  const float *cent_q, *cent_k;
+  const int32_t *size_q, *size_k;
+  int32_t bh, nq, nk, d;
+  double scale, theta;
+  const uint8_t *cand;   // [nq][nk] shared by all slices, or nullptr
+  uint8_t *mask;
+  int32_t *kept_count, *kept_idx;
+};
+hipError_t launch_select_threshold(const ThresholdArgs &a, hipStream_t s);
+
+constexpr int kMaxRadialDt = 15;        // largest temporal distance of the radial set
+constexpr int kMaxRadialRow = 8192;     // LDS capacity for one query block's kept list
+struct RadialParams {
+  int32_t n, hw, block, nb, dt_max, window0;
+  float ratio[kMaxRadialDt + 1];
+};
+hipError_t launch_radial_mask(const RadialParams &p, int32_t bh, uint8_t *mask,
+                              int32_t *kept_count, int32_t *kept_idx, hipStream_t s);
+hipError_t launch_block_means(const void *x, int32_t dtype, int32_t bh, int32_t n, int32_t d,
+                              int32_t block, float *means, int32_t *sizes, hipStream_t s);
+
 hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t s);
 
 constexpr int kMaxClustersSort = 16384;   // LDS counter capacity of the sort

@@ -33,9 +33,12 @@ class SparseVideoAttention:
     def __init__(self, batch: int, heads: int, n: int, d: int, cq: int, ck: int, iters: int,
                  top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda",
                  scale: Optional[float] = None, want_lse: bool = False,
-                 fuse_permutation: bool = True):
+                 fuse_permutation: bool = True, theta: Optional[float] = None):
         self.shape = (batch, heads, n, d)
         self.fused = fuse_permutation
+        # theta given: DynamicRad's dynamic threshold on the centroid logits
+        # replaces the cumulative top-p (the same candidates: all cluster pairs)
+        self.theta = theta
         self.cq, self.ck, self.iters, self.top_p = cq, ck, iters, top_p
         # a float32-representable scale, so the fp64 selection and the fp32
         # attention kernels use the identical value
@@ -95,8 +98,13 @@ class SparseVideoAttention:
         self._sort_kv(k, v, self.ws)
 
     def select(self):
-        L.sva_select_blocks(self.cent_q, self.sizes_q, self.cent_k, self.sizes_k, self.scale,
-                            self.top_p, self.mask, self.kept_count, self.kept_idx)
+        if self.theta is None:
+            L.sva_select_blocks(self.cent_q, self.sizes_q, self.cent_k, self.sizes_k, self.scale,
+                                self.top_p, self.mask, self.kept_count, self.kept_idx)
+        else:
+            L.sva_select_threshold(self.cent_q, self.sizes_q, self.cent_k, self.sizes_k,
+                                   self.scale, self.theta, None, self.mask, self.kept_count,
+                                   self.kept_idx)
 
     def attend(self, q=None, k=None, v=None):
         """Attention over the kept blocks; the fused path needs the original
@@ -148,3 +156,88 @@ class SparseVideoAttention:
         sk = self.sizes_k.cpu().numpy().astype(np.int64)
         m = self.mask.cpu().numpy().astype(np.int64)
         return int(np.einsum("bhi,bhij,bhj->", sq, m, sk))
+
+
+class RadialSparseAttention:
+    """DynamicRad-style block-sparse attention on uniform token blocks
+    (DynamicRad explainer, technical summary section 2.a).
+
+    One radial candidate set over blocks of ``block`` consecutive tokens of the
+    frame-major grid (hw tokens per frame), and one of two exclusive modes:
+
+    * ``"static"`` (throughput-first): per temporal distance dt, a fixed share
+      ``ratios[dt]`` of the candidates, nearest first.  The mask depends on the
+      geometry only, so it is built once here; ``forward`` is attention alone.
+    * ``"dynamic"`` (quality-first): block means of Q and K as proxies, pairs of
+      the candidate set whose proxy logit reaches ``theta`` are kept, and a
+      query block left empty keeps its best candidate.  ``forward`` runs block
+      means -> threshold -> attention.
+
+    Buffers are allocated once; ``forward`` allocates nothing and never
+    synchronises.
+    """
+
+    def __init__(self, batch: int, heads: int, n: int, d: int, hw: int, block: int = 128,
+                 mode: str = "static", ratios=(1.0, 1.0, 1.0), dt_max: int = 2, window0: int = 8,
+                 theta: Optional[float] = None, dtype: torch.dtype = torch.bfloat16,
+                 device="cuda", scale: Optional[float] = None, want_lse: bool = False):
+        if mode not in ("static", "dynamic"):
+            raise ValueError("mode must be 'static' or 'dynamic'")
+        if mode == "dynamic" and theta is None:
+            raise ValueError("the dynamic mode needs theta")
+        self.shape = (batch, heads, n, d)
+        self.mode, self.theta, self.block = mode, theta, block
+        self.scale = float(np.float32(1.0 / math.sqrt(d) if scale is None else scale))
+        dev = torch.device(device)
+        nb = -(-n // block)
+        self.nb = nb
+        off = torch.clamp(torch.arange(nb + 1, dtype=torch.int32, device=dev) * block, max=n)
+        self.off = off.expand(batch, heads, nb + 1).contiguous()
+        if mode == "static":
+            self.mask, self.kept_count, self.kept_idx = L.sva_radial_mask(
+                n, hw, block, dt_max, window0, list(ratios), batch, heads, dev)
+        else:
+            cand, _, _ = L.sva_radial_mask(n, hw, block, dt_max, window0, [1.0] * (dt_max + 1),
+                                           1, 1, dev)
+            self.cand = cand[0, 0].contiguous()
+            f32 = dict(dtype=torch.float32, device=dev)
+            i32 = dict(dtype=torch.int32, device=dev)
+            self.mean_q = torch.empty((batch, heads, nb, d), **f32)
+            self.mean_k = torch.empty((batch, heads, nb, d), **f32)
+            self.size_q = torch.empty((batch, heads, nb), **i32)
+            self.size_k = torch.empty((batch, heads, nb), **i32)
+            self.mask = torch.empty((batch, heads, nb, nb), dtype=torch.uint8, device=dev)
+            self.kept_count = torch.empty((batch, heads, nb), **i32)
+            self.kept_idx = torch.empty((batch, heads, nb, nb), **i32)
+        self.o = torch.empty(self.shape, dtype=dtype, device=dev)
+        self.lse = (torch.empty((batch, heads, n), dtype=torch.float32, device=dev)
+                    if want_lse else None)
+        lib = L.lib()
+        self.ws = torch.empty(max(lib.sva_attn_workspace_bytes(batch, heads, n, nb), 1),
+                              dtype=torch.uint8, device=dev)
+
+    def select(self, q, k):
+        """Dynamic mode: block means and the threshold selection (no-op when static)."""
+        if self.mode == "dynamic":
+            L.sva_block_means(q, self.block, self.mean_q, self.size_q)
+            L.sva_block_means(k, self.block, self.mean_k, self.size_k)
+            L.sva_select_threshold(self.mean_q, self.size_q, self.mean_k, self.size_k, self.scale,
+                                   self.theta, self.cand, self.mask, self.kept_count,
+                                   self.kept_idx)
+
+    def attend(self, q, k, v):
+        L.sva_block_sparse_attn(q, k, v, self.off, self.off, self.kept_count, self.kept_idx,
+                                self.scale, o=self.o, lse=self.lse, ws=self.ws)
+
+    def forward(self, q, k, v) -> torch.Tensor:
+        self.select(q, k)
+        self.attend(q, k, v)
+        return self.o
+
+    __call__ = forward
+
+    def kept_pairs(self) -> int:
+        """(query, key) token pairs the mask allows; synchronises."""
+        sizes = (self.off[0, 0, 1:] - self.off[0, 0, :-1]).cpu().numpy().astype(np.int64)
+        m = self.mask.cpu().numpy().astype(np.int64)
+        return int(np.einsum("i,bhij,j->", sizes, m, sizes))

@@ -91,6 +91,36 @@ def test_select_validation(L):
         assert lib.sva_select_blocks(*args) == want, (i, bad)
 
 
+def test_dynamicrad_validation(L):
+    lib = L.lib()
+    ok = (P, P, 10, P, P, 20, 1, 2, 128, 0.1, 0.5, None, P, P, P, None)
+    for i, bad, want in [(0, None, L.SVA_EINVAL), (2, 0, L.SVA_EINVAL), (5, 5000, L.SVA_EUNSUPPORTED),
+                         (8, 96, L.SVA_EUNSUPPORTED), (9, float("inf"), L.SVA_EINVAL),
+                         (10, float("nan"), L.SVA_EINVAL), (14, None, L.SVA_EINVAL)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.sva_select_threshold(*args) == want, (i, bad)
+    ratios = (ctypes.c_float * 3)(1.0, 0.5, 0.25)
+    bad_ratios = (ctypes.c_float * 3)(1.0, 1.5, 0.25)
+    rp = ctypes.cast(ratios, ctypes.c_void_p)
+    ok = [32760, 1560, 128, 2, 8, rp, 1, 2, P, P, P, None]
+    for i, bad, want in [(0, 0, L.SVA_EINVAL), (1, 0, L.SVA_EINVAL), (2, 0, L.SVA_EINVAL),
+                         (3, -1, L.SVA_EINVAL), (3, 16, L.SVA_EINVAL), (4, -1, L.SVA_EINVAL),
+                         (5, None, L.SVA_EINVAL),
+                         (5, ctypes.cast(bad_ratios, ctypes.c_void_p), L.SVA_EINVAL),
+                         (1, 1 << 30, L.SVA_EUNSUPPORTED), (8, None, L.SVA_EINVAL)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.sva_radial_mask(*args) == want, (i, bad)
+    ok = [P, 1, 1, 2, 1000, 128, 64, P, P, None]
+    for i, bad, want in [(0, None, L.SVA_EINVAL), (1, 7, L.SVA_EINVAL), (4, 0, L.SVA_EINVAL),
+                         (5, 32, L.SVA_EUNSUPPORTED), (6, 0, L.SVA_EINVAL), (8, None, L.SVA_EINVAL)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.sva_block_means(*args) == want, (i, bad)
+    assert "sva_block_means" in L.last_error()
+
+
 def test_attention_validation(L):
     lib = L.lib()
     ws = lib.sva_attn_workspace_bytes(1, 2, 1000, 8)
