@@ -90,6 +90,15 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="5s", choices=["5s", "10s", "30s"])
     ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--workload", default="svg2",
+                    choices=["svg2", "static-ratio", "dynamic-threshold"],
+                    help="svg2: k-means clusters + top-p (the default); static-ratio / "
+                         "dynamic-threshold: DynamicRad's two modes on uniform 128-token blocks")
+    ap.add_argument("--theta", type=float, default=None,
+                    help="svg2: global threshold on centroid logits instead of top-p; "
+                         "dynamic-threshold: threshold on block-mean logits (default 0)")
+    ap.add_argument("--ratios", default="1,0.75,0.5",
+                    help="static-ratio: kept share of the radial candidates per temporal distance")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -111,6 +120,8 @@ def main() -> int:
     import synth
     from sparse_attention_long_head_amd import SparseVideoAttention, sva_full_attn
 
+    if args.workload != "svg2":
+        return bench_dynamicrad(args)
     cfg = synth.CONFIGS[args.config]
     if args.top_p is not None:
         cfg = cfg.with_(top_p=args.top_p)
@@ -124,7 +135,8 @@ def main() -> int:
     ik = torch.from_numpy(init_k).to(dev)
     del x
     layer = SparseVideoAttention(cfg.batch, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters,
-                                 cfg.top_p, device=dev, fuse_permutation=not args.unfused)
+                                 cfg.top_p, device=dev, fuse_permutation=not args.unfused,
+                                 theta=args.theta)
     # "cluster" = k-means + permutation of Q (side stream) and of K/V, joined
     stages = ("cluster", "select", "attention", "unpermute")
 
@@ -221,7 +233,7 @@ def main() -> int:
         "config": {"workload": f"svg2 sparse attention layer, {cfg.name} clip",
                    "tokens": cfg.n, "grid_thw": [cfg.T, cfg.H, cfg.W], "heads": cfg.heads,
                    "head_dim": cfg.d, "batch": cfg.batch, "cq": cfg.cq, "ck": cfg.ck,
-                   "kmeans_iters": cfg.iters, "top_p": cfg.top_p,
+                   "kmeans_iters": cfg.iters, "top_p": cfg.top_p, "theta": args.theta,
                    "fused_permutation": not args.unfused, "centre_scale": cfg.alpha,
                    "density": round(density, 5), "kept_pairs": kept},
         "ms_per_layer": round(ms_step, 4),
@@ -234,6 +246,128 @@ def main() -> int:
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _timed(stages, step, steps, warmup):
+    """Run warmup + timed steps with per-stage events; returns (ms/step, per-stage medians)."""
+    import torch
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = {name: statistics.median(events[s][i].elapsed_time(events[s][i + 1])
+                                   for s in range(steps)) for i, name in enumerate(stages)}
+    return ms, per, events
+
+
+def cpu_baseline_dynamicrad(cfg, x, workload, ratios, theta, heads=tuple(range(8))):
+    """The fp64 oracle on a bounded sample (a few heads of the same tensors):
+    each head's mask, then its masked attention; about 5-10 s of host time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    hw = cfg.H * cfg.W
+    scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
+    rows = np.arange(cfg.n)
+    flops = 0.0
+    t0 = time.perf_counter()
+    for h in heads:
+        q, k, v = (x[n][0, h].astype(np.float64) for n in "qkv")
+        if workload == "static-ratio":
+            mask = oracle.static_ratio_mask(cfg.n, hw, cfg.block, 2, 8, ratios)
+        else:
+            cand = oracle.radial_candidates(cfg.n, hw, cfg.block, 2, 8)
+            mq, sq = oracle.block_means(q, cfg.block)
+            mk, sk = oracle.block_means(k, cfg.block)
+            mask = oracle.threshold_select(oracle.centroid_scores(mq, mk, scale), sq, sk, theta,
+                                           cand).mask
+        oracle.block_sparse_attention(q, k, v, mask, cfg.block, scale, rows=rows)
+        sizes = np.diff(np.minimum(np.arange(mask.shape[0] + 1) * cfg.block, cfg.n))
+        flops += 4.0 * cfg.d * float((mask[rows // cfg.block] * sizes[None, :]).sum())
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(heads)} of {cfg.heads} heads: mask, then masked attention of all "
+                      f"{cfg.n} query rows in fp64 NumPy; {dt:.1f} s"}
+
+
+def bench_dynamicrad(args) -> int:
+    """DynamicRad's static-ratio or dynamic-threshold mode on uniform 128-token
+    blocks at the 5 s clip size; one step = (block means + threshold, dynamic
+    only) + block-sparse attention.  The static mask depends on geometry only
+    and is built once, outside the timed steps."""
+    import torch
+
+    import synth
+    from sparse_attention_long_head_amd import RadialSparseAttention
+
+    static = args.workload == "static-ratio"
+    # static: config 2's i.i.d. N(0,1) tensors; dynamic: the 5 s mixture tokens
+    cfg = synth.CONFIGS["static" if static else "5s"]
+    ratios = [float(r) for r in args.ratios.split(",")]
+    theta = 0.0 if args.theta is None else args.theta
+    dev = torch.device("cuda:0")
+    log(f"[bench] {args.workload}: generating {cfg.name}: {cfg.n} tokens x {cfg.heads} heads")
+    x = synth.video_qkv(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv"}
+    layer = RadialSparseAttention(cfg.batch, cfg.heads, cfg.n, cfg.d, cfg.H * cfg.W, cfg.block,
+                                  "static" if static else "dynamic", ratios=ratios,
+                                  dt_max=len(ratios) - 1, theta=theta, device=dev)
+    stages = ("select", "attention")
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        layer.select(t["q"], t["k"])
+        if ev is not None:
+            ev[1].record()
+        layer.attend(t["q"], t["k"], t["v"])
+        if ev is not None:
+            ev[2].record()
+
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    ms, per, events = _timed(stages, step, args.steps, args.warmup)
+    kept = layer.kept_pairs()
+    flops = 4.0 * cfg.d * kept
+    attn_ms = statistics.mean(events[s][1].elapsed_time(events[s][2]) for s in range(args.steps))
+    attn_tf = flops / (attn_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] fp64 oracle on a bounded sample (host cores)")
+        cpu = cpu_baseline_dynamicrad(cfg, x, args.workload, ratios, theta)
+    value = flops / (ms * 1e-3) / 1e12
+    density = kept / float(cfg.batch * cfg.heads * cfg.n * cfg.n)
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded video tokens (no dataset)",
+        "config": {"workload": f"dynamicrad {args.workload} on uniform {cfg.block}-token blocks, "
+                               f"5s clip geometry", "tokens": cfg.n,
+                   "grid_thw": [cfg.T, cfg.H, cfg.W], "heads": cfg.heads, "head_dim": cfg.d,
+                   "block": cfg.block, "dt_max": len(ratios) - 1, "window0": 8,
+                   "ratios": ratios if static else None, "theta": None if static else theta,
+                   "density": round(density, 5), "kept_pairs": kept},
+        "ms_per_layer": round(ms, 4),
+        "stages_ms_median": {k: round(v, 4) for k, v in per.items()},
+        "attention": {"ms": round(attn_ms, 4), "effective_tflops": round(attn_tf, 2),
+                      "frac_of_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
