@@ -33,8 +33,14 @@ class SparseVideoAttention:
     def __init__(self, batch: int, heads: int, n: int, d: int, cq: int, ck: int, iters: int,
                  top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda",
                  scale: Optional[float] = None, want_lse: bool = False,
-                 fuse_permutation: bool = True, theta: Optional[float] = None):
+                 fuse_permutation: bool = True, theta: Optional[float] = None,
+                 iters_warm: Optional[int] = None):
         self.shape = (batch, heads, n, d)
+        # centroid cache (Sparse VideoGen2, section 2.c): a call without
+        # initial centroids starts from the previous call's final ones and runs
+        # iters_warm Lloyd iterations instead of iters
+        self.iters_warm = iters if iters_warm is None else iters_warm
+        self.cached = False
         self.fused = fuse_permutation
         # theta given: DynamicRad's dynamic threshold on the centroid logits
         # replaces the cumulative top-p (the same candidates: all cluster pairs)
@@ -84,6 +90,7 @@ class SparseVideoAttention:
         self.cent_k.copy_(init_k)
         L.sva_kmeans(q, self.cq, self.iters, self.cent_q, self.assign_q, self.sizes_q, ws=self.ws)
         L.sva_kmeans(k, self.ck, self.iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
+        self.cached = True
 
     def _sort_q(self, q, ws):
         L.sva_permute(self.assign_q, self.cq, [] if self.fused else [q], self.perm_q, self.off_q,
@@ -125,23 +132,33 @@ class SparseVideoAttention:
         if not self.fused:
             L.sva_unpermute(self.o_p, self.perm_q, self.o)
 
-    def cluster(self, q, k, v, init_q, init_k):
+    def cluster(self, q, k, v, init_q=None, init_k=None):
         """k-means and permutation of Q (side stream) and of K, V (current
         stream), concurrently; returns with the current stream ordered after
-        both."""
+        both.  Without init_q / init_k the previous call's centroids seed the
+        clustering (warm start)."""
+        cold = init_q is not None
+        if cold != (init_k is not None):
+            raise ValueError("give both init_q and init_k, or neither (warm start)")
+        if not cold and not self.cached:
+            raise ValueError("a warm start needs a previous call")
+        iters = self.iters if cold else self.iters_warm
         cur = torch.cuda.current_stream(self.ws.device)
         self.side.wait_stream(cur)
         with torch.cuda.stream(self.side):
-            self.cent_q.copy_(init_q)
-            L.sva_kmeans(q, self.cq, self.iters, self.cent_q, self.assign_q, self.sizes_q,
+            if cold:
+                self.cent_q.copy_(init_q)
+            L.sva_kmeans(q, self.cq, iters, self.cent_q, self.assign_q, self.sizes_q,
                          ws=self.ws_q)
             self._sort_q(q, self.ws_q)
-        self.cent_k.copy_(init_k)
-        L.sva_kmeans(k, self.ck, self.iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
+        if cold:
+            self.cent_k.copy_(init_k)
+        L.sva_kmeans(k, self.ck, iters, self.cent_k, self.assign_k, self.sizes_k, ws=self.ws)
         self._sort_kv(k, v, self.ws)
         cur.wait_stream(self.side)
+        self.cached = True
 
-    def forward(self, q, k, v, init_q, init_k) -> torch.Tensor:
+    def forward(self, q, k, v, init_q=None, init_k=None) -> torch.Tensor:
         self.cluster(q, k, v, init_q, init_k)
         self.select()
         self.attend(q, k, v)

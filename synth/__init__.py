@@ -31,6 +31,12 @@ Generator recipe (per video, per tensor X in {Q, K, V}, per head):
 5. Rounded to bf16 (round to nearest even) for bf16 configs; fp32 otherwise.
 
 Token order is t-major: n = (t*H + y)*W + x.
+
+Denoising-step sequences (for the centroid cache, Sparse VideoGen2 explainer,
+technical summary section 2.c): the tensors at step s are
+X_s = round(X_0 + s * step_drift * Delta), with one seeded direction field
+Delta ~ N(0, 1) per element, so consecutive steps differ by a small, fixed
+perturbation while the cluster structure stays put.
 """
 from __future__ import annotations
 
@@ -40,7 +46,8 @@ from typing import Dict, Optional, Tuple
 
 import numpy as np
 
-STREAMS = ("voronoi", "centres_q", "centres_k", "centres_v", "drift", "noise", "init", "pad")
+STREAMS = ("voronoi", "centres_q", "centres_k", "centres_v", "drift", "noise", "init", "pad",
+           "denoise")
 
 
 @dataclass(frozen=True)
@@ -193,6 +200,28 @@ def video_qkv(cfg: VideoConfig, heads: Optional[Tuple[int, ...]] = None,
                 arr[b, j] = round_bf16(x) if cfg.dtype == "bf16" else x
         out[name] = arr
     return out
+
+
+def denoise_direction(cfg: VideoConfig, which: str,
+                      heads: Optional[Tuple[int, ...]] = None) -> np.ndarray:
+    """The drift direction Delta of one tensor across denoising steps, float32
+    [batch, len(heads), N, d], i.i.d. N(0, 1)."""
+    heads = tuple(range(cfg.heads)) if heads is None else tuple(heads)
+    w = {"q": 0, "k": 1, "v": 2}[which]
+    out = np.empty((cfg.batch, len(heads), cfg.n, cfg.d), dtype=np.float32)
+    for b in range(cfg.batch):
+        for j, h in enumerate(heads):
+            rng = _child(_stream(cfg.seed, "denoise"), w, b, h)
+            out[b, j] = rng.standard_normal((cfg.n, cfg.d), dtype=np.float32)
+    return out
+
+
+def at_denoise_step(x0: np.ndarray, delta: np.ndarray, step: int, step_drift: float,
+                    dtype: str = "bf16") -> np.ndarray:
+    """X_s = X_0 + s * step_drift * Delta, evaluated in float32 and rounded like
+    the config's tensors (the exact values both paths consume)."""
+    x = (x0 + np.float32(step * step_drift) * delta).astype(np.float32)
+    return round_bf16(x) if dtype == "bf16" else x
 
 
 def kmeans_init_indices(cfg: VideoConfig, which: str, c: int,

@@ -120,3 +120,43 @@ def test_full_size_lockstep_two_iterations(video_5s, name):
     print(f"\n{name}: tie mismatches {ties}, rows re-decided in fp64 {refined} "
           f"({refined / (2 * cfg.heads * cfg.n):.3%})")
     assert ties <= 10
+
+
+def test_warm_start_lockstep_bf16():
+    """The centroid cache (Sparse VideoGen2, section 2.c): the next denoising
+    step's k-means starts from this step's GPU centroids; every warm iteration
+    matches the oracle's Lloyd step in lockstep."""
+    cfg = synth.CONFIGS["5s"].with_(T=3, heads=2)
+    x0 = synth.video_qkv(cfg)["k"]
+    delta = synth.denoise_direction(cfg, "k")
+    c = 300
+    init = synth.gather_init(x0, synth.kmeans_init_indices(cfg, "k", c))
+    cent = to_dev(init)
+    sva_kmeans(to_dev(x0, torch.bfloat16), c, cfg.iters, cent)
+    warm = host(cent)
+    x1 = synth.at_denoise_step(x0, delta, 1, 0.05)
+    ties, _ = _lockstep(x1, warm, c, 3, torch.bfloat16)
+    assert ties <= 2
+
+
+def test_layer_warm_start_equals_explicit_init():
+    from sparse_attention_long_head_amd import SparseVideoAttention
+    cfg = synth.CONFIGS["5s"].with_(T=3, heads=2)
+    x = synth.video_qkv(cfg)
+    dq, dk = synth.denoise_direction(cfg, "q"), synth.denoise_direction(cfg, "k")
+    iq = to_dev(synth.gather_init(x["q"], synth.kmeans_init_indices(cfg, "q", 40)))
+    ik = to_dev(synth.gather_init(x["k"], synth.kmeans_init_indices(cfg, "k", 200)))
+    t0 = {n: to_dev(x[n], torch.bfloat16) for n in "qkv"}
+    t1 = {"q": to_dev(synth.at_denoise_step(x["q"], dq, 1, 0.05), torch.bfloat16),
+          "k": to_dev(synth.at_denoise_step(x["k"], dk, 1, 0.05), torch.bfloat16), "v": t0["v"]}
+    a = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, 40, 200, 10, 0.9, device=device(),
+                             iters_warm=3)
+    with pytest.raises(ValueError):
+        a(t0["q"], t0["k"], t0["v"])                      # nothing cached yet
+    a(t0["q"], t0["k"], t0["v"], iq, ik)
+    cq, ck = a.cent_q.clone(), a.cent_k.clone()
+    o_warm = a(t1["q"], t1["k"], t1["v"]).clone()      # warm: 3 iterations from the cache
+    b = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, 40, 200, 3, 0.9, device=device())
+    o_cold = b(t1["q"], t1["k"], t1["v"], cq, ck)
+    assert torch.equal(o_warm, o_cold)
+    assert torch.equal(a.assign_k, b.assign_k) and torch.equal(a.cent_q, b.cent_q)

@@ -66,3 +66,15 @@ def test_ell_encoding():
 def test_uniform_offsets_ragged_tail():
     off = synth.uniform_offsets(300, 128)
     assert off.tolist() == [0, 128, 256, 300]
+
+
+def test_denoise_steps_are_a_fixed_drift():
+    cfg = synth.CONFIGS["5s"].with_(T=2, heads=2)
+    x0 = synth.video_qkv(cfg)["q"]
+    d1 = synth.denoise_direction(cfg, "q")
+    d2 = synth.denoise_direction(cfg, "q", heads=(1,))
+    assert np.array_equal(d1[:, 1:], d2)                 # stateless per head
+    assert np.array_equal(synth.at_denoise_step(x0, d1, 0, 0.05), x0)
+    x2 = synth.at_denoise_step(x0, d1, 2, 0.05, dtype="f32")
+    np.testing.assert_allclose(x2 - x0, 0.1 * d1, atol=1e-5)
+    assert abs(float(d1.std()) - 1.0) < 0.01
