@@ -91,11 +91,13 @@ def main() -> int:
     ap.add_argument("--config", default="5s", choices=["5s", "10s", "30s"])
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--workload", default="svg2",
-                    choices=["svg2", "static-ratio", "dynamic-threshold", "kmeans-warm"],
+                    choices=["svg2", "static-ratio", "dynamic-threshold", "kmeans-warm", "sweep"],
                     help="svg2: k-means clusters + top-p (the default); static-ratio / "
                          "dynamic-threshold: DynamicRad's two modes on uniform 128-token blocks; "
                          "kmeans-warm: the svg2 layer over a drifting denoising sequence with the "
                          "centroid cache (warm-started k-means)")
+    ap.add_argument("--sweep-p", default="0.8,0.9,0.95")
+    ap.add_argument("--sweep-alpha", default="1.5,1.75,2.0")
     ap.add_argument("--denoise-steps", type=int, default=4)
     ap.add_argument("--step-drift", type=float, default=0.05)
     ap.add_argument("--warm-iters", type=int, default=2,
@@ -128,6 +130,8 @@ def main() -> int:
 
     if args.workload == "kmeans-warm":
         return bench_kmeans_warm(args)
+    if args.workload == "sweep":
+        return bench_sweep(args)
     if args.workload != "svg2":
         return bench_dynamicrad(args)
     cfg = synth.CONFIGS[args.config]
@@ -378,6 +382,85 @@ def bench_dynamicrad(args) -> int:
                      "traffic": None},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_sweep(args) -> int:
+    """Density / error / time over top-p x centre scale alpha (the content's
+    cluster separation) on one clip config: for every alpha the clip is drawn
+    anew and dense attention is the reference; for every p the whole layer is
+    timed and its output compared with dense (relative L2 error over all heads,
+    both bf16 outputs of this library)."""
+    import torch
+
+    import synth
+    from sparse_attention_long_head_amd import SparseVideoAttention, sva_full_attn
+
+    base = synth.CONFIGS[args.config]
+    ps = [float(v) for v in args.sweep_p.split(",")]
+    alphas = [float(v) for v in args.sweep_alpha.split(",")]
+    dev = torch.device("cuda:0")
+    rows = []
+    dense_ms = None
+    for alpha in alphas:
+        cfg = base.with_(alpha=alpha)
+        log(f"[bench] sweep {cfg.name}: alpha {alpha}: generating {cfg.n} x {cfg.heads}")
+        x = synth.video_qkv(cfg)
+        iq = torch.from_numpy(synth.gather_init(x["q"], synth.kmeans_init_indices(cfg, "q", cfg.cq))).to(dev)
+        ik = torch.from_numpy(synth.gather_init(x["k"], synth.kmeans_init_indices(cfg, "k", cfg.ck))).to(dev)
+        t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv"}
+        del x
+        layer = SparseVideoAttention(cfg.batch, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck,
+                                     cfg.iters, ps[0], device=dev)
+        o_dense = torch.empty_like(t["q"])
+        sva_full_attn(t["q"], t["k"], t["v"], layer.scale, o=o_dense)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sva_full_attn(t["q"], t["k"], t["v"], layer.scale, o=o_dense)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1)
+        dn = float(o_dense.float().norm())
+        for p in ps:
+            layer.top_p = p
+            stages = ("cluster", "select", "attention")
+
+            def step(ev):
+                if ev is not None:
+                    ev[0].record()
+                layer.cluster(t["q"], t["k"], t["v"], iq, ik)
+                if ev is not None:
+                    ev[1].record()
+                layer.select()
+                if ev is not None:
+                    ev[2].record()
+                layer.attend(t["q"], t["k"], t["v"])
+                if ev is not None:
+                    ev[3].record()
+
+            ms, per, _ = _timed(stages, step, max(2, min(args.steps, 5)), 1)
+            kept = layer.kept_pairs()
+            density = kept / float(cfg.batch * cfg.heads * cfg.n * cfg.n)
+            err = float((layer.o.float() - o_dense.float()).norm()) / dn
+            rows.append({"alpha": alpha, "top_p": p, "density": round(density, 5),
+                         "ms_layer": round(ms, 3), "ms_attention": round(per["attention"], 3),
+                         "ms_dense_attention": round(dense_ms, 3),
+                         "speedup_attention": round(dense_ms / per["attention"], 3),
+                         "speedup_layer": round(dense_ms / ms, 3),
+                         "effective_tflops_attention":
+                             round(4.0 * cfg.d * kept / (per["attention"] * 1e-3) / 1e12, 1),
+                         "rel_l2_error_vs_dense": round(err, 5)})
+            log(f"[bench]   p {p}: density {density:.4f}, layer {ms:.2f} ms, "
+                f"attention {per['attention']:.2f} ms, rel err {err:.4f}")
+        del layer, t, o_dense
+        torch.cuda.empty_cache()
+    out = {"metric": "density / error / time sweep over top-p x alpha", "config":
+           {"workload": f"svg2 layer sweep, {base.name} clip", "tokens": base.n,
+            "heads": base.heads, "cq": base.cq, "ck": base.ck, "kmeans_iters": base.iters},
+           "data": "synthetic: seeded mixture-of-Gaussians video tokens (no dataset)",
+           "rows": rows}
     print(json.dumps(out), flush=True)
     return 0
 
