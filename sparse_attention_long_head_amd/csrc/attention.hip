@@ -525,47 +525,57 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
         dst[i] = v < L ? sStart[lo] + (v - sCum[lo]) : -1;
       }
     };
-    // PERM: wave 0 copies the original rows of chunk c's keys into the chunk's
-    // stage (from row 0 past the end, so every step issues one copy)
-    auto rowmap = [&](int c, auto st) {
+    // PERM: the original rows of a chunk's keys reach the chunk's sPerm stage
+    // in two steps: wave 0 loads them into a register (a plain global load, a
+    // step ahead), then stores the register into the stage.  sPerm is thus an
+    // ordinary LDS array, and reading it needs no wait on the K/V copies in
+    // flight.  Past the end of the list the row of key 0 stands in.
+    int pnext = 0;
+    auto perm_load = [&](int c) {
       if constexpr (PERM) {
         if (wave == 0) {
           const int rr = c * kKT < L ? sWin[(c / kWin) & 1][(c % kWin) * kKT + lane] : -1;
-          const int32_t *src = pbase + (rr < 0 ? 0 : rr);
-          __builtin_amdgcn_global_load_lds(
-              src, (__attribute__((address_space(3))) void *)&sPerm[decltype(st)::value][0], 4, 0, 0);
+          pnext = pbase[rr < 0 ? 0 : rr];
         }
       }
     };
-    // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
-    auto issue_loads = [&](auto st, int cc) {
+    auto perm_store = [&](auto st) {
+      if constexpr (PERM) {
+        if (wave == 0) sPerm[decltype(st)::value][lane] = pnext;
+      }
+    };
+    // the K/V source rows of this lane's copies of chunk cc (in stage st): the
+    // row map, then (PERM) the original rows.  Past the end of the list (the
+    // chunks after the last) whole stages are refilled from key 0's row, so
+    // every step issues the same number of copies.  Read a step before the
+    // copies are issued, so the LDS latency hides behind that step's compute.
+    struct ChunkRows {
+      int phys[LPW];
+    };
+    auto fetch_rows = [&](auto st, int cc) {
+      ChunkRows cr;
       const bool live = cc * kKT < L;   // uniform
       const int32_t *rows = sWin[(cc / kWin) & 1] + (cc % kWin) * kKT;
+      const int32_t *prow = sPerm[decltype(st)::value];
+      const int dummy = PERM ? prow[0] : (live ? max(rows[0], 0) : 0);
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int r = RPI * (wave * LPW + j) + ld_rsub;
+        int phys = live ? rows[r] : -1;
+        if constexpr (PERM) phys = phys < 0 ? -1 : prow[r];
+        cr.phys[j] = phys < 0 ? dummy : phys;
+      }
+      return cr;
+    };
+    // issue the asynchronous HBM -> LDS copies of one chunk's K and V rows
+    auto issue_loads = [&](auto st, const ChunkRows &cr) {
       uint16_t *dk = sK[decltype(st)::value];
       uint16_t *dv = sV[decltype(st)::value];
-      // past the end of the list (the chunks after the last) whole stages are
-      // refilled from key row 0, so every step issues the same number of copies
-      int dummy = live ? max(rows[0], 0) : 0;
-      int prow[LPW];
-      if constexpr (PERM) {   // original rows of this lane's keys (and of key 0)
-        const uint32_t pb = lds_offset(&sPerm[decltype(st)::value][0]);
-        uint32_t pa[LPW + 1];
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) pa[j] = pb + 4 * (RPI * (wave * LPW + j) + ld_rsub);
-        pa[LPW] = pb;
-        int pv[LPW + 1];
-        lds_read_i32s(pv, pa);
-        dummy = live && rows[0] >= 0 ? pv[LPW] : 0;
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) prow[j] = pv[j];
-      }
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int blk = wave * LPW + j;
         const int r = RPI * blk + ld_rsub;
-        int phys = live ? rows[r] : -1;
-        if constexpr (PERM) phys = phys < 0 ? -1 : prow[j];
-        phys = phys < 0 ? dummy : phys;
+        const int phys = cr.phys[j];
         // (offsets stay in named variables: with an arithmetic expression in the
         // builtin's argument list, hipcc 7.2's host pass emits no launch stub)
         const int koff = phys * D + ((ld_piece ^ kswz<D>(r)) << 3);
@@ -579,18 +589,25 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       }
     };
 
-    // prologue: row-map windows 0 and 1, chunks 0 and 1 in flight (and, PERM,
-    // the original rows of chunk 2 on their way)
+    // prologue: row-map windows 0 and 1; (PERM) the original rows of chunks
+    // 0-3 in their stages and chunk 4's loaded; chunks 0 and 1 in flight and
+    // chunk 2's source rows in registers
     build_win(0);
     if (kWin < nch) build_win(1);
     __syncthreads();
-    rowmap(0, std::integral_constant<int, 0>{});
-    rowmap(1, std::integral_constant<int, 1>{});
-    rowmap(2, std::integral_constant<int, 2>{});
-    if constexpr (PERM) wait_vmcnt<1>();   // original rows of chunks 0, 1 landed (wave 0)
+    perm_load(0);
+    perm_store(std::integral_constant<int, 0>{});
+    perm_load(1);
+    perm_store(std::integral_constant<int, 1>{});
+    perm_load(2);
+    perm_store(std::integral_constant<int, 2>{});
+    perm_load(3);
+    perm_store(std::integral_constant<int, 3>{});
+    perm_load(4);
     lds_barrier();
-    issue_loads(std::integral_constant<int, 0>{}, 0);
-    issue_loads(std::integral_constant<int, 1>{}, 1);
+    issue_loads(std::integral_constant<int, 0>{}, fetch_rows(std::integral_constant<int, 0>{}, 0));
+    issue_loads(std::integral_constant<int, 1>{}, fetch_rows(std::integral_constant<int, 1>{}, 1));
+    ChunkRows nxt = fetch_rows(std::integral_constant<int, 2>{}, 2);
 
     // S^T = K Q^T for the 64 keys of the chunk in stage ST (two 32-key m-tiles)
     // x the wave's query tiles; each K fragment serves every query tile
@@ -715,13 +732,15 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       // chunk c has landed once only chunk c+1's copies are outstanding; after
       // the barrier every wave's copies of chunk c are in LDS and every wave is
       // done with chunk c-2, whose stage chunk c+2 then refills
-      // (PERM: wave 0's copy of the original rows of chunk c+2 is older than
-      // chunk c+1's K/V copies, so it has landed too)
+      // (PERM: wave 0's load of chunk c+4's original rows is older than chunk
+      // c+1's K/V copies, so it has landed too)
       wait_vmcnt<2 * LPW>();
       lds_barrier();
       if (c % kWin == 0 && (c / kWin + 1) * kWin < nch) build_win(c / kWin + 1);
-      rowmap(c + 3, std::integral_constant<int, (S + 3) % kStages>{});
-      issue_loads(std::integral_constant<int, (S + 2) % kStages>{}, c + 2);
+      perm_store(st);                 // chunk c+4 (its stage is chunk c's)
+      perm_load(c + 5);
+      issue_loads(std::integral_constant<int, (S + 2) % kStages>{}, nxt);
+      nxt = fetch_rows(std::integral_constant<int, (S + 3) % kStages>{}, c + 3);
 
       if (wave_active) {
         if (late && c > 0) softmax(c - 1);
