@@ -179,10 +179,15 @@ __device__ __forceinline__ int fetch_work(int32_t *ctl, int &gone) {
 //   items: per slice, one item per tile, in block order (the fp32 kernel walks
 //          these directly); plus the slice's cost sum and item count
 //   order: one workgroup deals slices to the 8 XCDs (largest first, each to
-//          the least loaded) and sorts each XCD's items by descending cost;
-//          the bf16 kernel's persistent workgroups take them from these queues
-//          (longest processing time first) and steal from other XCDs' queues
-//          when their own is empty
+//          the least loaded); each XCD's queue holds its slices one after
+//          another in the order they were dealt, every slice's items by
+//          descending cost.  The XCD's compute units then work on one slice
+//          at a time, so that slice's K/V (16.8 MB at 32,760 tokens, d = 128)
+//          stays in the memory-side cache while its items run instead of
+//          competing with the K/V of every other slice of the XCD; the last
+//          slices still end longest processing time first.  The bf16 kernel's
+//          persistent workgroups take items from these queues and steal from
+//          other XCDs' queues when their own is empty
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attn_cost_kernel(
     const int32_t *__restrict__ k_off, const int32_t *__restrict__ kept_count,
@@ -257,10 +262,21 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
   __shared__ int32_t s_x[kMaxOrderHeads];            // XCD of each slice
   __shared__ int32_t s_order[kMaxOrderHeads];        // slices by descending cost
   __shared__ int32_t s_hist[8][kOrderBuckets];       // counts, then write cursors
+  __shared__ int32_t s_rank[kMaxOrderHeads];         // position among its XCD's slices
   __shared__ int32_t s_cnt[8], s_start[8];
+  __shared__ int32_t s_group;                        // slices per sort group
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const bool balance = nbh <= kMaxOrderHeads;
   auto xcd_of = [&](int h) { return balance ? s_x[h] : (h & 7); };
+  // sort key, ascending = earlier in the queue: the slice's group (up to 8
+  // groups of consecutive ranks), then the cost, descending, in kOrderBuckets/8
+  // buckets (exact below 3/4 of them, then 16 chunks per bucket)
+  constexpr int kCB = kOrderBuckets / 8, kExact = kCB * 3 / 4;
+  auto key = [&](const WorkItem &it) {
+    if (!balance) return kOrderBuckets - 1 - min(it.cost, kOrderBuckets - 1);
+    const int c = it.cost < kExact ? it.cost : min(kExact + (it.cost - kExact) / 16, kCB - 1);
+    return (s_rank[it.bh] / s_group) * kCB + (kCB - 1 - c);
+  };
   for (int i = t; i < 8 * kOrderBuckets; i += kOrderThreads) (&s_hist[0][0])[i] = 0;
   if (balance) {
     // rank of each slice by (cost desc, index asc), then a greedy deal
@@ -276,31 +292,36 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
     __syncthreads();
     if (t == 0) {
       long long load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      int dealt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int r = 0; r < nbh; ++r) {
         const int h = s_order[r];
         int best = 0;
         for (int x = 1; x < 8; ++x) best = load[x] < load[best] ? x : best;
         s_x[h] = best;
+        s_rank[h] = dealt[best]++;
         load[best] += hinfo[2 * h];
       }
+      int most = 1;
+      for (int x = 0; x < 8; ++x) most = max(most, dealt[x]);
+      s_group = (most + 7) / 8;
     }
   }
   __syncthreads();
-  // histogram of item costs per XCD
+  // histogram of the item keys per XCD
   const size_t total = static_cast<size_t>(nbh) * work_cap;
   for (size_t i = t; i < total; i += kOrderThreads) {
     const WorkItem it = work[i];
     if (it.qb < 0) continue;
-    atomicAdd(&s_hist[xcd_of(it.bh)][min(it.cost, kOrderBuckets - 1)], 1);
+    atomicAdd(&s_hist[xcd_of(it.bh)][key(it)], 1);
   }
   __syncthreads();
-  // per XCD, exclusive scan in descending cost order (wave x scans XCD x)
+  // per XCD, exclusive scan in key order (wave x scans XCD x)
   if (wave < 8) {
     constexpr int PER = kOrderBuckets / 64;
     int v[PER], sum = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {           // lane's buckets, descending cost
-      v[j] = s_hist[wave][kOrderBuckets - 1 - (lane * PER + j)];
+    for (int j = 0; j < PER; ++j) {           // the lane's buckets
+      v[j] = s_hist[wave][lane * PER + j];
       sum += v[j];
     }
     int x = sum;
@@ -312,7 +333,7 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
     int run = x - sum;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      s_hist[wave][kOrderBuckets - 1 - (lane * PER + j)] = run;
+      s_hist[wave][lane * PER + j] = run;
       run += v[j];
     }
     if (lane == 63) s_cnt[wave] = x;
@@ -330,7 +351,7 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
     const WorkItem it = work[i];
     if (it.qb < 0) continue;
     const int x = xcd_of(it.bh);
-    const int pos = atomicAdd(&s_hist[x][min(it.cost, kOrderBuckets - 1)], 1);
+    const int pos = atomicAdd(&s_hist[x][key(it)], 1);
     lists[s_start[x] + pos] = it;
   }
   if (t < 8) {
