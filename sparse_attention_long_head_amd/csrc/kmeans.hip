@@ -644,7 +644,10 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
   __shared__ double s_part[WPC > 1 ? WPC : 1][WPC > 1 ? D : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wc = WPC > 1 ? wave : 0;         // this wave's rank within its cluster
-  const int cl = WPC > 1 ? blockIdx.x : blockIdx.x * kMeanWaves + wave, bh = blockIdx.y;
+  // slices in reverse launch order: the assign pass just before walked them in
+  // ascending order, so the last ones it read are the likeliest still cached
+  const int cl = WPC > 1 ? blockIdx.x : blockIdx.x * kMeanWaves + wave;
+  const int bh = gridDim.y - 1 - blockIdx.y;
   if (cl >= ncl) return;                     // uniform over the cluster's waves
   const bool real = cl < c;
   const int g = lane / TPR, pc = lane % TPR;
