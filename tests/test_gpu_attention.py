@@ -129,6 +129,38 @@ def test_variable_blocks(bf16, seed):
         check_lse(lse[0, h], rl, 1e-3 if bf16 else 1e-5)
 
 
+def test_many_slices_per_xcd():
+    # 3 x 30 = 90 slices: up to 12 dealt to one XCD, so the work queues group
+    # two slices per sort group; every slice must still be complete and exact
+    rng = np.random.default_rng(21)
+    b, heads, d, nq, nk, nqb, nkb = 3, 30, 64, 300, 260, 5, 7
+    q = rand_inputs((b, heads, nq, d), 70, "bf16")
+    k = rand_inputs((b, heads, nk, d), 71, "bf16")
+    v = rand_inputs((b, heads, nk, d), 72, "bf16")
+    qoff = np.stack([np.stack([_random_partition(nq, nqb, rng) for _ in range(heads)])
+                     for _ in range(b)])
+    koff = np.stack([np.stack([_random_partition(nk, nkb, rng) for _ in range(heads)])
+                     for _ in range(b)])
+    masks = rng.random((b, heads, nqb, nkb)) < 0.5
+    masks[..., 0] = True
+    cnt, idx = synth.mask_to_ell(masks)
+    T = _tdtype(True)
+    scale = 1 / math.sqrt(d)
+    o, lse = sva_block_sparse_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T),
+                                   to_dev(qoff, torch.int32), to_dev(koff, torch.int32),
+                                   to_dev(cnt, torch.int32), to_dev(idx, torch.int32), scale,
+                                   want_lse=True)
+    o, lse = host(o), host(lse)
+    for bi in range(b):
+        for h in range(heads):
+            aq = np.repeat(np.arange(nqb), np.diff(qoff[bi, h]))
+            ak = np.repeat(np.arange(nkb), np.diff(koff[bi, h]))
+            ro, rl = oracle.cluster_sparse_attention(q[bi, h], k[bi, h], v[bi, h], aq, ak,
+                                                     masks[bi, h], np.float32(scale))
+            check_attention(o[bi, h], ro, True, f"slice {bi},{h}")
+            check_lse(lse[bi, h], rl, 1e-3)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_one_key_blocks_and_empty_blocks(bf16):
     # every kept key block holds one key or none: a 64-key chunk then spans 64
