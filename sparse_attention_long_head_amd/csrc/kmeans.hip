@@ -533,47 +533,26 @@ __global__ __launch_bounds__(kThreads, 2) void km_refine_kernel(
 
 // ---------------------------------------------------------------------------
 // refine queue of a slice: the per-tile regions of tflags joined in tile order
-// into flags[0, total); total goes to qcount[slice].  One workgroup per slice.
+// into flags[0, total); total goes to qcount[slice].  One wave per tile: it
+// adds up the counts of the tiles before its own (its offset), then copies its
+// region; the wave of the last tile writes the total.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void km_queue_join_kernel(
     const int2 *__restrict__ tflags, const int32_t *__restrict__ tcount, int n, int tph,
     int2 *__restrict__ flags, int32_t *__restrict__ qcount) {
-  __shared__ int32_t s_cnt[kThreads];
-  __shared__ int32_t s_pre[kThreads];
-  __shared__ int32_t s_w[kThreads / 64];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int2 *src = tflags + static_cast<size_t>(bh) * n;
-  int2 *dst = flags + static_cast<size_t>(bh) * n;
-  int base = 0;
-  for (int t0 = 0; t0 < tph; t0 += kThreads) {
-    const int cnt = t0 + tid < tph ? tcount[static_cast<size_t>(bh) * tph + t0 + tid] : 0;
-    int x = cnt;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (t >= tph) return;   // wave-uniform
+  const int32_t *cnt = tcount + static_cast<size_t>(bh) * tph;
+  int pre = 0;
+  for (int u = lane; u < t; u += 64) pre += cnt[u];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) s_w[wave] = x;
-    s_cnt[tid] = cnt;
-    __syncthreads();
-    int pre = x - cnt, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-      pre += w < wave ? s_w[w] : 0;
-      tot += s_w[w];
-    }
-    s_pre[tid] = base + pre;
-    __syncthreads();
-    // one wave per tile region, lanes over its entries
-    for (int t = wave; t < kThreads && t0 + t < tph; t += kThreads / 64) {
-      const int c = s_cnt[t], o = s_pre[t];
-      const int2 *from = src + static_cast<size_t>(t0 + t) * kTokTile;
-      for (int j = lane; j < c; j += 64) dst[o + j] = from[j];
-    }
-    base += tot;
-    __syncthreads();
-  }
-  if (tid == 0) qcount[bh] = base;
+  for (int o = 32; o > 0; o >>= 1) pre += __shfl_xor(pre, o);
+  const int c = cnt[t];
+  const int2 *from = tflags + static_cast<size_t>(bh) * n + static_cast<size_t>(t) * kTokTile;
+  int2 *to = flags + static_cast<size_t>(bh) * n + pre;
+  for (int j = lane; j < c; j += 64) to[j] = from[j];
+  if (t == tph - 1 && lane == 0) qcount[bh] = pre + c;
 }
 
 // ---------------------------------------------------------------------------
@@ -808,8 +787,8 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
                          static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
                          a.assign, tflags, tcount, a.bh, tph);
       SVA_CHECK(hipGetLastError());
-      hipLaunchKernelGGL(km_queue_join_kernel, dim3(a.bh), dim3(kThreads), 0, s, tflags, tcount,
-                         a.n, tph, flags, ctl);
+      hipLaunchKernelGGL(km_queue_join_kernel, dim3((tph + kThreads / 64 - 1) / (kThreads / 64), a.bh),
+                         dim3(kThreads), 0, s, tflags, tcount, a.n, tph, flags, ctl);
       SVA_CHECK(hipGetLastError());
       hipLaunchKernelGGL((km_refine_kernel<D>), tok_grid, dim3(kThreads), 0, s,
                          static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, ctl,

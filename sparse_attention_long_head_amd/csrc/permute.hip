@@ -8,10 +8,12 @@
 //      same cluster earlier in the tile (wave ballots over the key bits give
 //      the equal-key mask; the 4 waves of a step add to LDS counters in order)
 //      and the tile's cluster histogram, stored cluster-major.
-//   2. scan: one exclusive scan over [cluster][tile] per slice gives the first
-//      permuted row of every (cluster, tile) pair, the cluster offsets and the
-//      cluster sizes.
-//   3. scatter: perm[base(cluster, tile) + rank] = row.
+//   2. scan_rows: one wave per cluster: the exclusive scan of its row of tile
+//      counts (the cluster's first permuted row of each tile, relative to the
+//      cluster) and the cluster's size, in parallel over every (slice, cluster).
+//   3. scan_totals: per slice, the exclusive scan of the cluster sizes gives the
+//      cluster offsets (and the sizes when asked).
+//   4. scatter: perm[offset(cluster) + base(cluster, tile) + rank] = row.
 // Integer work only, so the result is exact and deterministic.
 #include "../../include/sva.h"
 #include "sva_internal.h"
@@ -60,57 +62,90 @@ __global__ __launch_bounds__(kThreads) void sort_hist_rank_kernel(
   for (int cl = tid; cl < c; cl += kThreads) hh[static_cast<size_t>(cl) * tiles + tile] = cnt[cl];
 }
 
-__global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(
-    const int32_t *__restrict__ hist, int n, int c, int tiles, int32_t *__restrict__ base,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sizes, int32_t *__restrict__ clear) {
+// one wave per (slice, cluster): row [cluster][0, tiles) of the histogram
+// -> base (exclusive, relative to the cluster) and the row total, which goes
+// to offsets[cluster] for scan_totals to turn into the cluster's offset
+__global__ __launch_bounds__(kThreads) void sort_scan_rows_kernel(
+    const int32_t *__restrict__ hist, int c, int tiles, int32_t *__restrict__ base,
+    int32_t *__restrict__ offsets) {
+  const int cl = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (cl >= c) return;   // wave-uniform
+  const size_t row = (static_cast<size_t>(bh) * c + cl) * tiles;
+  int carry = 0;
+  for (int t0 = 0; t0 < tiles; t0 += 64) {
+    const int t = t0 + lane;
+    const int v = t < tiles ? hist[row + t] : 0;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (t < tiles) base[row + t] = carry + x - v;
+    carry += __shfl(x, 63);
+  }
+  if (lane == 0) offsets[static_cast<size_t>(bh) * (c + 1) + cl] = carry;
+}
+
+// per slice: offsets[0, c) holds the cluster sizes; replaced in place by their
+// exclusive scan (4 consecutive clusters per thread per round), offsets[c] = n
+__global__ __launch_bounds__(kScanThreads) void sort_scan_totals_kernel(
+    int n, int c, int32_t *__restrict__ offsets, int32_t *__restrict__ sizes,
+    int32_t *__restrict__ clear) {
   __shared__ int32_t wsum[kScanThreads / 64];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t len = static_cast<size_t>(c) * tiles;
-  const int32_t *hh = hist + static_cast<size_t>(bh) * len;
-  int32_t *bb = base + static_cast<size_t>(bh) * len;
-  const size_t seg = (len + kScanThreads - 1) / kScanThreads;
-  const size_t s0 = min(len, seg * tid), s1 = min(len, s0 + seg);
-  int sum = 0;
-  for (size_t e = s0; e < s1; ++e) sum += hh[e];
-  int x = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int run = x - sum;
-  for (int w = 0; w < wave; ++w) run += wsum[w];
   int32_t *off = offsets + static_cast<size_t>(bh) * (c + 1);
-  for (size_t e = s0; e < s1; ++e) {
-    bb[e] = run;
-    if (e % tiles == 0) off[e / tiles] = run;
-    run += hh[e];
+  int32_t *sz = sizes != nullptr ? sizes + static_cast<size_t>(bh) * c : nullptr;
+  int carry = 0;
+  for (int r0 = 0; r0 < c; r0 += 4 * kScanThreads) {
+    const int e0 = r0 + 4 * tid;
+    int v[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = e0 + j < c ? off[e0 + j] : 0;
+      sum += v[j];
+    }
+    int x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int run = carry + x - sum, tot = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      run += w < wave ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e0 + j < c) {
+        if (sz != nullptr) sz[e0 + j] = v[j];
+        off[e0 + j] = run;
+        run += v[j];
+      }
+    carry += tot;
+    __syncthreads();   // wsum is reused by the next round
   }
   if (tid == 0) {
     off[c] = n;
     if (clear != nullptr) clear[bh] = 0;   // a per-slice counter of the caller
   }
-  if (sizes != nullptr) {
-    int32_t *sz = sizes + static_cast<size_t>(bh) * c;
-    for (int cl = tid; cl < c; cl += kScanThreads) {
-      int s = 0;
-      for (int t = 0; t < tiles; ++t) s += hh[static_cast<size_t>(cl) * tiles + t];
-      sz[cl] = s;
-    }
-  }
 }
 
 __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
     const int32_t *__restrict__ assign, const int32_t *__restrict__ rank,
-    const int32_t *__restrict__ base, int n, int c, int tiles, int32_t *__restrict__ perm) {
+    const int32_t *__restrict__ base, const int32_t *__restrict__ offsets, int n, int c,
+    int tiles, int32_t *__restrict__ perm) {
   const int bh = blockIdx.y;
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
   const size_t row = static_cast<size_t>(bh) * n + i;
   const int key = min(max(assign[row], 0), c - 1);   // as in hist_rank
-  const int pos = base[(static_cast<size_t>(bh) * c + key) * tiles + i / kTile] + rank[row];
+  const int pos = offsets[static_cast<size_t>(bh) * (c + 1) + key] +
+                  base[(static_cast<size_t>(bh) * c + key) * tiles + i / kTile] + rank[row];
   perm[static_cast<size_t>(bh) * n + pos] = i;
 }
 
@@ -164,12 +199,16 @@ hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int
                      static_cast<size_t>(c) * 4, s, assign, n, c, tiles, bits_for(c), hist, rank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(bh), dim3(kScanThreads), 0, s, hist, n, c, tiles,
-                     base, offsets, sizes, clear);
+  hipLaunchKernelGGL(sort_scan_rows_kernel, dim3((c + kThreads / 64 - 1) / (kThreads / 64), bh),
+                     dim3(kThreads), 0, s, hist, c, tiles, base, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sort_scan_totals_kernel, dim3(bh), dim3(kScanThreads), 0, s, n, c, offsets,
+                     sizes, clear);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3((n + kThreads - 1) / kThreads, bh),
-                     dim3(kThreads), 0, s, assign, rank, base, n, c, tiles, perm);
+                     dim3(kThreads), 0, s, assign, rank, base, offsets, n, c, tiles, perm);
   return hipGetLastError();
 }
 
