@@ -9,14 +9,20 @@
 //   clusters on the accumulator rows and tokens on lanes; the accumulator
 //   starts at -||c||^2/2, so no VALU op is spent on it.  x is exactly bf16 and
 //   every fp32 centroid is split into bf16 hi + lo (residual <= 2^-16 |c|).
-//   Each lane keeps the best and second-best w of its clusters (max + med3)
-//   and the best index; the two lane halves merge.  Every w carries a rigorous
+//   Each lane keeps the three best w of its clusters (max + two med3) and the
+//   tiles of the best two; the two lane halves merge.  Every w carries a rigorous
 //   error bound E (split residual + fp32 accumulation of 2d exact products and
 //   the start value + final rounding, from ||x|| and max ||c||).  A row whose
-//   best two w are more than 2E apart is decided; any other row is queued
-//   with the threshold best - 2E (each token tile writes its queued rows to a
-//   region of its own; a join kernel concatenates the regions in tile order,
-//   so there are no atomics and the queue order is deterministic).
+//   best two w are more than 2E apart is decided.  A row whose third-best w
+//   is more than 2E below its best has exactly two candidates (no other
+//   cluster can be the argmin): it goes to the pair list of its token tile
+//   and is settled by two fp64 distances.  Any other row is queued with the
+//   threshold best - 2E (each token tile writes its queued rows to the front
+//   of a region of its own and its pairs to the back; a join kernel
+//   concatenates the queue parts in tile order, so there are no atomics and
+//   the queue order is deterministic).
+// pair: one thread per listed row computes the exact fp64 distances to its two
+//   candidates; the smaller wins, ties to the lower index.
 // refine: queued rows run through the same MFMA loop; every cluster with
 //   w >= threshold (a set that provably holds the true argmin) goes to an LDS
 //   candidate list; one wave per candidate computes the exact fp64 distance,
@@ -54,7 +60,7 @@ __device__ __forceinline__ int cswz(int r) {
 }
 
 struct KmLayout {
-  size_t chi, clo, nh, ctl, flags, tflags, tcount, perm, offsets, sort, total;
+  size_t chi, clo, nh, ctl, flags, tflags, tcount, pcount, perm, offsets, sort, total;
 };
 
 // ctl holds the bh refine-queue lengths
@@ -74,6 +80,7 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   L.flags = take(static_cast<size_t>(bh) * n * 8);
   L.tflags = take(static_cast<size_t>(bh) * n * 8);
   L.tcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
+  L.pcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
   L.perm = take(static_cast<size_t>(bh) * n * 4);
   L.offsets = take(static_cast<size_t>(bh) * (c + 1) * 4);
   L.sort = take(sort_ws_bytes(bh, n, c));
@@ -88,12 +95,12 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
 // ring filled by direct global->LDS copies two tiles ahead; one partial vmcnt
 // wait and one barrier per tile.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool PAIRS>
 __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
     const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
     const uint16_t *__restrict__ clo, const float *__restrict__ nh,
     int32_t *__restrict__ assign, int2 *__restrict__ tflags, int32_t *__restrict__ tcount,
-    int nbh, int tph) {
+    int32_t *__restrict__ pcount, int nbh, int tph) {
   constexpr int NS = D / 16;
   constexpr int NT = kNT;
   constexpr int PPR = D / 8;                          // 16-byte pieces per centroid row
@@ -106,6 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sC[3][2][32 * D];
   __shared__ __attribute__((aligned(16))) float sN[3][64];   // [32, 64): copy padding
   __shared__ int32_t s_wq[kThreads / 64];
+  __shared__ int32_t s_wp[kThreads / 64];
   __shared__ float s_nhmin[kThreads / 64];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; slices are dealt
@@ -214,15 +222,17 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
   for (int s2 = 0; s2 < NS; ++s2) ka[s2] = sc0 + col * D * 2 + (((2 * s2 + h) ^ cswz<D>(col)) << 4);
   const uint32_t na = lds_offset(&sN[0][0]) + 16 * h;
 
-  // best and second-best w of the lane's clusters; the best's row within its
-  // tile rides in the 4 low mantissa bits of the tracked values, its tile in t1
-  float b1[NT], b2[NT];
-  int t1[NT];
+  // the three best w of the lane's clusters; each value's row within its tile
+  // rides in its 4 low mantissa bits, the tiles of the best two in t1, t2
+  float b1[NT], b2[NT], b3[NT];
+  int t1[NT], t2[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     b1[nt] = -INFINITY;
     b2[nt] = -INFINITY;
+    b3[nt] = -INFINITY;
     t1[nt] = 0;
+    t2[nt] = 0;
   }
 
   auto step = [&](auto st, int ct) {
@@ -254,17 +264,24 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
     }
     // w with its accumulator index i (0..15) in the 4 low mantissa bits: one
     // and-or, and max / med3 then carry the index along (the change of w,
-    // below 2^-19 |w|, is part of the error bound)
+    // below 2^-19 |w|, is part of the error bound).  Inserting we into
+    // b1 >= b2 >= b3: b3 = med3(b2, b3, we), b2 = med3(b1, b2, we), b1 = max.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float prev = b1[nt];
+      const float p1 = b1[nt], p2 = b2[nt];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float we = __int_as_float((__float_as_int(acc[nt][i]) & ~15) | i);
+        if constexpr (PAIRS) b3[nt] = __builtin_amdgcn_fmed3f(b2[nt], b3[nt], we);
         b2[nt] = __builtin_amdgcn_fmed3f(b1[nt], b2[nt], we);
         b1[nt] = __builtin_elementwise_maximum(b1[nt], we);
       }
-      t1[nt] = b1[nt] != prev ? ct : t1[nt];
+      // the second best is the old one, the demoted old best, or from this
+      // tile (a bit-equal value from another tile makes b3 == b2, and such a
+      // row is never settled from t2)
+      const bool new1 = b1[nt] != p1;
+      if constexpr (PAIRS) t2[nt] = b2[nt] == p2 ? t2[nt] : ((new1 && b2[nt] == p1) ? t1[nt] : ct);
+      t1[nt] = new1 ? ct : t1[nt];
     }
   };
   for (int ct = 0; ct < ntl; ct += 3) {
@@ -281,13 +298,15 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) nhmin = fminf(nhmin, s_nhmin[w]);
   const float cm = sqrtf(-2.f * nhmin) * (1.f + 0x1p-20f);
-  // decided rows are assigned; the others are compacted, in wave and lane
-  // order, into this tile's region of the slice's queue area (tflags), with
-  // their count in tcount; a join kernel then concatenates the regions
-  bool queued[NT];
-  uint64_t qm[NT];
-  int thr_bits[NT];
-  int wq = 0;
+  // decided rows are assigned; queued rows are compacted, in wave and lane
+  // order, to the front of this tile's region of the slice's queue area
+  // (tflags), pair rows (token, best, second; cluster ids below 2^16) to its
+  // back, with their counts in tcount and pcount
+  bool queued[NT], paired[NT];
+  uint64_t qm[NT], pm[NT];
+  int thr_bits[NT], pair_ids[NT];
+  int wq = 0, wp = 0;
+  const bool pairs_ok = PAIRS && c <= 65536;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx[nt] * cm +
@@ -295,36 +314,120 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
                     0x1p-19f * (nx[nt] * cm + 0.5f * cm * cm);
     const float two_e = 2.f * 1.25f * e;
     const int i1 = t1[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
+    const int i2 = t2[nt] * 32 + acc_row(__float_as_int(b2[nt]) & 15, h);
     const float ob1 = __shfl_xor(b1[nt], 32), ob2 = __shfl_xor(b2[nt], 32);
-    const int oi1 = __shfl_xor(i1, 32);
+    const float ob3 = __shfl_xor(b3[nt], 32);
+    const int oi1 = __shfl_xor(i1, 32), oi2 = __shfl_xor(i2, 32);
     const bool other = ob1 > b1[nt] || (ob1 == b1[nt] && oi1 < i1);
     const float nb1 = fmaxf(b1[nt], ob1);
     const int ival = other ? oi1 : i1;
-    const float nb2 = fmaxf(fminf(b1[nt], ob1), fmaxf(b2[nt], ob2));
+    // second best: the smaller of the two bests or the larger of the two
+    // seconds; third best of the six (each lane's three sorted)
+    const float lo1 = fminf(b1[nt], ob1), hi2 = fmaxf(b2[nt], ob2);
+    const float nb2 = fmaxf(lo1, hi2);
+    const int ival2 = lo1 >= hi2 ? (other ? i1 : oi1) : (b2[nt] >= ob2 ? i2 : oi2);
+    const float nb3 = fmaxf(fmaxf(fminf(b1[nt], ob2), fminf(b2[nt], ob1)), fmaxf(b3[nt], ob3));
     const bool decided = nb1 - nb2 > two_e;
+    const bool two = !decided && pairs_ok && nb1 - nb3 > two_e;
     if (h == 0 && tv[nt] && decided) assign[static_cast<size_t>(bh) * n + tok[nt]] = ival;
-    queued[nt] = h == 0 && tv[nt] && !decided;
+    queued[nt] = h == 0 && tv[nt] && !decided && !two;
+    paired[nt] = h == 0 && tv[nt] && two;
     thr_bits[nt] = __float_as_int(nb1 - two_e);
+    pair_ids[nt] = (ival << 16) | ival2;
     qm[nt] = __ballot(queued[nt]);
+    pm[nt] = __ballot(paired[nt]);
     wq += __popcll(qm[nt]);
+    wp += __popcll(pm[nt]);
   }
-  if (lane == 0) s_wq[wave] = wq;
+  if (lane == 0) {
+    s_wq[wave] = wq;
+    s_wp[wave] = wp;
+  }
   __syncthreads();
-  int q = base, tot = 0;
+  int q = base, p = 0, tot = 0, ptot = 0;
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) {
     q += w < wave ? s_wq[w] : 0;
+    p += w < wave ? s_wp[w] : 0;
     tot += s_wq[w];
+    ptot += s_wp[w];
   }
+  // the region's last row: pair k sits at [last - k]
+  const int last = base + min(kTokTile, n - base) - 1;
   const uint64_t lt = (1ull << lane) - 1;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (queued[nt])
       tflags[static_cast<size_t>(bh) * n + q + __popcll(qm[nt] & lt)] = int2{tok[nt], thr_bits[nt]};
+    if (paired[nt])
+      tflags[static_cast<size_t>(bh) * n + last - (p + __popcll(pm[nt] & lt))] =
+          int2{tok[nt], pair_ids[nt]};
     q += __popcll(qm[nt]);
+    p += __popcll(pm[nt]);
   }
-  if (tid == 0) tcount[static_cast<size_t>(bh) * tph + tile] = tot;
+  if (tid == 0) {
+    tcount[static_cast<size_t>(bh) * tph + tile] = tot;
+    pcount[static_cast<size_t>(bh) * tph + tile] = ptot;
+  }
 }
+
+// ---------------------------------------------------------------------------
+// pair rows: the rows listed at the back of a token tile's region (one
+// workgroup per tile, as the main pass), D/8 lanes per row (each lane 8 consecutive dimensions); exact fp64 squared distances
+// to the two candidates, each lane's 8 terms added in ascending dimension
+// order and the lanes' partial sums then in a fixed butterfly; the smaller
+// distance wins, ties to the lower index.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void km_pair_kernel(
+    const uint16_t *__restrict__ x, int n, int c, const float *__restrict__ cent,
+    const int2 *__restrict__ tflags, const int32_t *__restrict__ pcount,
+    int32_t *__restrict__ assign, int32_t *__restrict__ n_refined, int nbh, int tph) {
+  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (k8 / tph);
+  const int tile = k8 % tph;
+  if (bh >= nbh) return;
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPW = 64 / LPR;              // rows per wave pass
+  constexpr int RPB = RPW * (kThreads / 64); // rows per workgroup pass
+  const int np = pcount[static_cast<size_t>(bh) * tph + tile];
+  const int base = tile * kTokTile;
+  const int last = base + min(kTokTile, n - base) - 1;
+  const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;                // this lane's 8 dimensions
+  const int rw = wave * RPW + lane / LPR;    // this lane's row within a pass
+  for (int k0 = 0; k0 < np; k0 += RPB) {
+    const int k = k0 + rw;
+    const bool live = k < np;                // uniform over the row's lanes
+    const int2 e = tflags[static_cast<size_t>(bh) * n + last - (live ? k : 0)];
+    const int ids[2] = {(e.y >> 16) & 0xffff, e.y & 0xffff};
+    const u32x4 xv = reinterpret_cast<const u32x4 *>(xb + static_cast<size_t>(e.x) * D)[sub];
+    double dist[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const f32x4 *cr = reinterpret_cast<const f32x4 *>(cent + (static_cast<size_t>(bh) * c + ids[r]) * D);
+      const f32x4 c0 = cr[2 * sub], c1 = cr[2 * sub + 1];
+      double s = 0.0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float xf32 = bf16_bits_to_f32(static_cast<uint16_t>(xv[t >> 1] >> (16 * (t & 1))));
+        const float cf32 = t < 4 ? c0[t] : c1[t - 4];
+        const double df = static_cast<double>(xf32) - static_cast<double>(cf32);
+        s = fma(df, df, s);
+      }
+#pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      dist[r] = s;
+    }
+    if (live && sub == 0) {
+      const bool second = dist[1] < dist[0] || (dist[1] == dist[0] && ids[1] < ids[0]);
+      assign[static_cast<size_t>(bh) * n + e.x] = second ? ids[1] : ids[0];
+    }
+  }
+  if (n_refined != nullptr && threadIdx.x == 0 && np > 0) atomicAdd(n_refined, np);
+}
+
 // ---------------------------------------------------------------------------
 // fp64 refinement of the queued rows: the queued rows run through the same
 // MFMA loop (centroid tiles staged through registers into two LDS buffers);
@@ -742,6 +845,7 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   int2 *flags = reinterpret_cast<int2 *>(w + L.flags);
   int2 *tflags = reinterpret_cast<int2 *>(w + L.tflags);
   int32_t *tcount = reinterpret_cast<int32_t *>(w + L.tcount);
+  int32_t *pcount = reinterpret_cast<int32_t *>(w + L.pcount);
   int32_t *perm = reinterpret_cast<int32_t *>(w + L.perm);
   int32_t *offsets = reinterpret_cast<int32_t *>(w + L.offsets);
   void *sort_ws = w + L.sort;
@@ -783,9 +887,22 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   for (int it = 0; it < a.iters; ++it) {
     const bool last = it + 1 == a.iters;
     if (bf16) {
-      hipLaunchKernelGGL((km_assign_main_kernel<D>), tok_grid, dim3(kThreads), 0, s,
-                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
-                         a.assign, tflags, tcount, a.bh, tph);
+      // the pair path (third best tracked) pays once the refine's re-scan is
+      // long: with 8 or more centroid tiles
+      const bool pairs = cpad >= 8 * 32;
+      if (pairs)
+        hipLaunchKernelGGL((km_assign_main_kernel<D, true>), tok_grid, dim3(kThreads), 0, s,
+                           static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
+                           a.assign, tflags, tcount, pcount, a.bh, tph);
+      else
+        hipLaunchKernelGGL((km_assign_main_kernel<D, false>), tok_grid, dim3(kThreads), 0, s,
+                           static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
+                           a.assign, tflags, tcount, pcount, a.bh, tph);
+      SVA_CHECK(hipGetLastError());
+      if (pairs)
+        hipLaunchKernelGGL((km_pair_kernel<D>), tok_grid, dim3(kThreads), 0, s,
+                           static_cast<const uint16_t *>(a.x), a.n, a.c, a.centroids, tflags,
+                           pcount, a.assign, a.n_refined, a.bh, tph);
       SVA_CHECK(hipGetLastError());
       hipLaunchKernelGGL(km_queue_join_kernel, dim3((tph + kThreads / 64 - 1) / (kThreads / 64), a.bh),
                          dim3(kThreads), 0, s, tflags, tcount, a.n, tph, flags, ctl);
