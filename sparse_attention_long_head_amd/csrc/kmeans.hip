@@ -720,7 +720,7 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
   constexpr int EPT = 16 / EB;               // elements per 16-byte piece
   constexpr int TPR = D / EPT;               // lanes per row
   constexpr int RG = 64 / TPR;               // row groups per wave
-  constexpr int U = (64 / RG) < 16 ? (64 / RG) : 16;   // rows in flight per lane
+  constexpr int U = (64 / RG) < 8 ? (64 / RG) : 8;   // rows in flight per lane (8: more waves fit)
   static_assert(TPR <= 64 && 64 % TPR == 0 && (64 / RG) % U == 0, "row layout");
   static_assert(WPC == 1 || WPC == kMeanWaves, "waves per cluster");
   __shared__ double s_part[WPC > 1 ? WPC : 1][WPC > 1 ? D : 1];
