@@ -61,6 +61,38 @@ def test_small_video_lockstep_bf16(d, c):
     assert ties <= 2
 
 
+def test_pair_path_with_duplicate_centroids():
+    # 300 clusters (10 centroid tiles: the two-candidate path is on) with one
+    # centroid doubled and one tripled, in different tiles and at the same row
+    # of a tile (bit-equal w with equal row bits): rows nearest a doubled
+    # centroid are two-candidate rows that tie exactly (the lower id wins),
+    # rows nearest the tripled one have three candidates (refine pass)
+    cfg = synth.CONFIGS["5s"].with_(T=2, heads=2)             # 3,120 tokens
+    x = synth.video_qkv(cfg)["k"]
+    c = 300
+    init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "k", c)).copy()
+    for h in range(2):
+        init[0, h, 32 + 7] = init[0, h, 7]                    # same row of tiles 0 and 1
+        init[0, h, 96 + 20] = init[0, h, 20]
+        init[0, h, 160 + 20] = init[0, h, 20]
+        init[0, h, 250] = init[0, h, 77]                      # another row, another tile
+    n_ref = torch.zeros(1, dtype=torch.int32, device=device())
+    cent = to_dev(init.astype(np.float32))
+    _, assign, _ = sva_kmeans(to_dev(x, torch.bfloat16), c, 1, cent, n_refined=n_ref)
+    a = host(assign)
+    ties = 0
+    for h in range(2):
+        ref, margin = oracle.assign_step(x[0, h].astype(np.float64), init[0, h].astype(np.float64))
+        ties += assign_parity(a[0, h], ref, margin, f"head {h}")
+        # the duplicates tie exactly: the lowest id must win on the GPU too
+        dup = np.isin(ref, [7, 20, 77])
+        assert dup.sum() >= 3, "the duplicated clusters must own some rows"
+        assert np.array_equal(a[0, h][dup], ref[dup]), (h, np.flatnonzero(a[0, h][dup] != ref[dup]))
+        assert not np.isin(a[0, h], [32 + 7, 96 + 20, 160 + 20, 250]).any()
+    assert ties <= 2
+    assert int(n_ref.item()) > 0
+
+
 def test_empty_cluster_keeps_centroid_and_c_equals_n():
     dev = device()
     rng = np.random.default_rng(0)
