@@ -927,7 +927,9 @@ hipError_t run_f32(const AttnArgs &a, const WorkItem *work, int cap, int n_items
   return hipGetLastError();
 }
 
-// compute units of the current device (the persistent grid), cached per device
+}  // namespace
+
+// compute units of the current device (persistent grids), cached per device
 int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -940,8 +942,6 @@ int device_cus() {
   if (dev < 64) cached[dev] = cus;
   return cus;
 }
-
-}  // namespace
 
 size_t attn_ws_bytes(int32_t bh, int32_t n_q, int32_t nqb) {
   return sched_layout(bh, n_q, nqb).total;

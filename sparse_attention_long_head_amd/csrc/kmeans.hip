@@ -53,6 +53,9 @@ constexpr int kThreads = 256;
 constexpr int kNT = 3;                          // 32-token tiles per wave
 constexpr int kTokTile = kNT * 32 * (kThreads / 64);   // tokens per workgroup (384)
 constexpr int kCandCap = 3072;                  // refine candidates staged per batch
+constexpr int kResTok = 64;                     // tokens per tile of the resident pass
+constexpr int kResWaves = 8;                    // waves per workgroup of the resident pass
+constexpr int kResTiles = 4;                    // centroid tiles (of 32) it holds per slice
 
 template <int D>
 __device__ __forceinline__ int cswz(int r) {
@@ -79,7 +82,7 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   L.ctl = take(static_cast<size_t>(bh) * 4);
   L.flags = take(static_cast<size_t>(bh) * n * 8);
   L.tflags = take(static_cast<size_t>(bh) * n * 8);
-  L.tcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
+  L.tcount = take(static_cast<size_t>(bh) * ((n + kResTok - 1) / kResTok) * 4);   // either pass
   L.pcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
   L.perm = take(static_cast<size_t>(bh) * n * 4);
   L.offsets = take(static_cast<size_t>(bh) * (c + 1) * 4);
@@ -372,6 +375,242 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MFMA assignment, main pass with the centroid table resident (at most
+// kResTiles tiles of 32 clusters).  A slice's whole table (hi and lo splits
+// plus -||c||^2/2) fits in LDS, so a persistent workgroup loads it once and
+// its waves then run with no barrier: wave w takes the 64-token tiles
+// t0 + w, t0 + w + 8, ... of the workgroup's range [t0, t1), loading the next
+// tile's rows into a second register buffer while the current tile's MFMAs
+// run.  A range never covers more than two consecutive slices (the grid has
+// at least one workgroup per slice), and both tables are loaded up front.
+// Arithmetic, error bound and queue rows are those of the streaming pass;
+// each 64-token tile has its own queue region and count.
+// ---------------------------------------------------------------------------
+// v from lane l ^ 32: permlane32_swap exchanges lanes 32-63 of its first
+// operand with lanes 0-31 of its second
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+template <int D, int NTL>
+__global__ __launch_bounds__(64 * kResWaves, 1) void km_assign_res_kernel(
+    const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
+    const uint16_t *__restrict__ clo, const float *__restrict__ nh,
+    int32_t *__restrict__ assign, int2 *__restrict__ tflags, int32_t *__restrict__ tcount,
+    int nbh, int tph) {
+  constexpr int NS = D / 16;
+  constexpr int PPR = D / 8;                       // 16-byte pieces per centroid row
+  constexpr int ROWS = NTL * 32;
+  constexpr int kSplitB = ROWS * D * 2;            // bytes of one split of a slot
+  constexpr int kThr = 64 * kResWaves;
+  __shared__ __attribute__((aligned(16))) uint16_t sC[2][2][ROWS * D];
+  __shared__ __attribute__((aligned(16))) float sN[2][ROWS];
+  __shared__ float s_min[2][kResWaves];
+  __shared__ float s_cm[2];
+
+  const long long tt = static_cast<long long>(nbh) * tph;
+  const int t0 = static_cast<int>(tt * blockIdx.x / gridDim.x);
+  const int t1 = static_cast<int>(tt * (blockIdx.x + 1) / gridDim.x);
+  if (t0 >= t1) return;   // uniform over the workgroup
+  const int s0 = t0 / tph, ns = (t1 - 1) / tph - s0 + 1;   // 1 or 2 slices
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar tile bookkeeping
+  const int h = lane >> 5, col = lane & 31;
+
+  // the tile's rows: B operands of 32x32x16 MFMAs, lane holds
+  // x[token][16 s + 8 h .. +8] of token base + 32 nt + col
+  auto load = [&](bf16x8 (&xf)[2][NS], int t) {
+    const int sl = t / tph, base = (t % tph) * kResTok;
+    const uint16_t *xb = x + static_cast<size_t>(sl) * n * D;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int tok = min(base + nt * 32 + col, n - 1);
+      const uint16_t *row = xb + static_cast<size_t>(tok) * D + h * 8;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+        xf[nt][s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + s2 * 16));
+    }
+  };
+
+  // the first tile's rows are in flight while the tables load (a wave with
+  // no tile loads its range's first tile and leaves after the barriers)
+  int gt = t0 + wave;
+  bf16x8 xa[2][NS], xb[2][NS];
+  load(xa, gt < t1 ? gt : t0);
+
+  // both tables, k-major: piece p = 2 s + h (dimensions 8p .. 8p+7) of row r
+  // sits at 16-byte slot (s * ROWS + r) * 2 + h of its split, so a wave's
+  // fragment read for one k-step is 1 KB of consecutive bytes.  Thread idx
+  // fills slot idx (consecutive lanes, consecutive LDS bytes).
+  for (int k = 0; k < ns; ++k) {
+    const size_t cbase = static_cast<size_t>(s0 + k) * cpad;
+    for (int idx = tid; idx < 2 * ROWS * PPR; idx += kThr) {
+      const int sp = idx / (ROWS * PPR), slot = idx % (ROWS * PPR);
+      const int hh = slot & 1, r = (slot >> 1) % ROWS, s2 = (slot >> 1) / ROWS;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>((sp ? clo : chi) + (cbase + r) * D +
+                                                       (2 * s2 + hh) * 8);
+      *reinterpret_cast<u32x4 *>(&sC[k][sp][slot * 8]) = v;
+    }
+    float mn = 0.f;
+    for (int j = tid; j < ROWS; j += kThr) {
+      const float v = nh[cbase + j];
+      sN[k][j] = v;
+      if (j < c) mn = fminf(mn, v);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
+    if (lane == 0) s_min[k][wave] = mn;
+  }
+  __syncthreads();
+  // each slot's bound: max ||c|| of the slice's real clusters (with margin)
+  if (tid < 2) {
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < kResWaves; ++w) m = fminf(m, tid < ns ? s_min[tid][w] : 0.f);
+    s_cm[tid] = sqrtf(-2.f * m) * (1.f + 0x1p-20f);
+  }
+  __syncthreads();
+
+  if (gt >= t1) return;   // wave-uniform; no barrier follows
+
+  auto tile_pass = [&](const bf16x8 (&xf)[2][NS], int t) {
+    const int sl = t / tph, tile = t % tph, k = sl - s0;
+    const int base = tile * kResTok;
+    // LDS byte address of this lane's A fragment (row col, piece h) of k-step
+    // 0 in the slot's split 0, tile 0; k-step s is ROWS * 32 bytes further
+    const uint32_t ka = lds_offset(&sC[k][0][0]) + (col * 2 + h) * 16;
+    const uint32_t na = lds_offset(&sN[k][0]) + 16 * h;
+    float b1[2], b2[2];
+    int t1r[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      b1[nt] = -INFINITY;
+      b2[nt] = -INFINITY;
+      t1r[nt] = 0;
+    }
+    f32x16 acc[2];
+    auto ctile = [&](auto ctc) {
+      constexpr int ct = decltype(ctc)::value;
+      f32x4 n4[4];                                  // -||c||^2/2 of the lane's 16 rows
+      lds_read_f32x4x4<ct * 128, 32>(n4, na);
+      f32x16 cinit;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cinit[4 * g + j] = n4[g][j];
+      // hi split for both token groups, then the lo split group by group, so
+      // that the first group's argmax tracking below runs under the second
+      // group's MFMAs
+      bf16x8 af[NS];
+      lds_read_frags_strided<ct * 1024, ROWS * 32>(af, ka);
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[nt] = mfma32x32x16(af[s2], xf[nt][s2], s2 == 0 ? cinit : acc[nt]);
+      lds_read_frags_strided<kSplitB + ct * 1024, ROWS * 32>(af, ka);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) acc[nt] = mfma32x32x16(af[s2], xf[nt][s2], acc[nt]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float p1 = b1[nt];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float we = __int_as_float((__float_as_int(acc[nt][i]) & ~15) | i);
+          b2[nt] = __builtin_amdgcn_fmed3f(b1[nt], b2[nt], we);
+          b1[nt] = __builtin_elementwise_maximum(b1[nt], we);
+        }
+        t1r[nt] = b1[nt] != p1 ? ct : t1r[nt];
+        // the tracking happens here: otherwise the compiler sinks it to the
+        // decisions and keeps every tile's accumulators alive until then
+        asm volatile("" : "+v"(b1[nt]), "+v"(b2[nt]), "+v"(t1r[nt]));
+      }
+      // schedule: the first group's lo MFMAs, then the second group's, each
+      // followed by an equal share of the first group's tracking; nothing
+      // moves across tiles (register budget)
+      __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 48 / NS, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    ctile(std::integral_constant<int, 0>{});
+    if constexpr (NTL > 1) ctile(std::integral_constant<int, 1>{});
+    if constexpr (NTL > 2) ctile(std::integral_constant<int, 2>{});
+    if constexpr (NTL > 3) ctile(std::integral_constant<int, 3>{});
+    // decisions, as in the streaming pass; queued rows compacted in lane order
+    const float cm = s_cm[k];
+    bool queued[2];
+    uint64_t qm[2];
+    int thr_bits[2], tok[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      tok[nt] = base + nt * 32 + col;
+      const bool tv = tok[nt] < n;
+      // ||x||^2 by bf16 pair dot products (exact products, fp32 sums); the
+      // 2^-60 covers products below the fp32 normal range if they are flushed
+      float p = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 u = __builtin_bit_cast(u32x4, xf[nt][s2]);
+          const uint32_t w = u[j];
+          const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+          p = __builtin_amdgcn_fdot2_f32_bf16(v, v, p, false);
+        }
+      p += xor32(p);
+      const float nx = sqrtf(p) * (1.f + 0x1p-10f) + 0x1p-60f;
+      const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx * cm +
+                      (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx * cm) +
+                      0x1p-19f * (nx * cm + 0.5f * cm * cm);
+      const float two_e = 2.f * 1.25f * e;
+      const int i1 = t1r[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
+      const float ob1 = xor32(b1[nt]), ob2 = xor32(b2[nt]);
+      const int oi1 = __float_as_int(xor32(__int_as_float(i1)));
+      const bool other = ob1 > b1[nt] || (ob1 == b1[nt] && oi1 < i1);
+      const float nb1 = fmaxf(b1[nt], ob1);
+      const float nb2 = fmaxf(fminf(b1[nt], ob1), fmaxf(b2[nt], ob2));
+      const bool decided = nb1 - nb2 > two_e;
+      if (h == 0 && tv && decided) assign[static_cast<size_t>(sl) * n + tok[nt]] = other ? oi1 : i1;
+      queued[nt] = h == 0 && tv && !decided;
+      thr_bits[nt] = __float_as_int(nb1 - two_e);
+      qm[nt] = __ballot(queued[nt]);
+    }
+    // rank among the queued lanes below this one
+    auto below = [](uint64_t m) {
+      return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    };
+    const size_t region = static_cast<size_t>(sl) * n + base;
+    if (queued[0]) tflags[region + below(qm[0])] = int2{tok[0], thr_bits[0]};
+    if (queued[1]) tflags[region + __popcll(qm[0]) + below(qm[1])] = int2{tok[1], thr_bits[1]};
+    if (lane == 0) tcount[static_cast<size_t>(sl) * tph + tile] = __popcll(qm[0]) + __popcll(qm[1]);
+  };
+
+  // two register buffers in turn; past the range end the current tile is
+  // loaded again (a cache hit) so the loads stay unconditional
+  for (;;) {
+    int nx = gt + kResWaves;
+    load(xb, nx < t1 ? nx : gt);
+    tile_pass(xa, gt);
+    if (nx >= t1) break;
+    gt = nx;
+    nx = gt + kResWaves;
+    load(xa, nx < t1 ? nx : gt);
+    tile_pass(xb, gt);
+    if (nx >= t1) break;
+    gt = nx;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // pair rows: the rows listed at the back of a token tile's region (one
 // workgroup per tile, as the main pass), D/8 lanes per row (each lane 8 consecutive dimensions); exact fp64 squared distances
 // to the two candidates, each lane's 8 terms added in ascending dimension
@@ -635,27 +874,56 @@ __global__ __launch_bounds__(kThreads, 2) void km_refine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// refine queue of a slice: the per-tile regions of tflags joined in tile order
-// into flags[0, total); total goes to qcount[slice].  One wave per tile: it
-// adds up the counts of the tiles before its own (its offset), then copies its
-// region; the wave of the last tile writes the total.
+// refine queue of a slice: the per-tile regions of tflags (rt rows apart)
+// joined in tile order into flags[0, total); total goes to qcount[slice].  A
+// workgroup takes kJoinTiles consecutive tiles: it adds up the counts of the
+// slice's earlier tiles, scans its own counts in one wave, and its threads
+// then copy the tiles' rows together; the workgroup with the last tile writes
+// the total.
 // ---------------------------------------------------------------------------
+constexpr int kJoinTiles = 64;
 __global__ __launch_bounds__(kThreads) void km_queue_join_kernel(
-    const int2 *__restrict__ tflags, const int32_t *__restrict__ tcount, int n, int tph,
+    const int2 *__restrict__ tflags, const int32_t *__restrict__ tcount, int n, int tph, int rt,
     int2 *__restrict__ flags, int32_t *__restrict__ qcount) {
-  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), bh = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  if (t >= tph) return;   // wave-uniform
+  __shared__ int32_t s_off[kJoinTiles + 1];
+  __shared__ int32_t s_part[kThreads / 64];
+  const int bh = blockIdx.y, t0 = blockIdx.x * kJoinTiles;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t *cnt = tcount + static_cast<size_t>(bh) * tph;
   int pre = 0;
-  for (int u = lane; u < t; u += 64) pre += cnt[u];
+  for (int u = tid; u < t0; u += kThreads) pre += cnt[u];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) pre += __shfl_xor(pre, o);
-  const int c = cnt[t];
-  const int2 *from = tflags + static_cast<size_t>(bh) * n + static_cast<size_t>(t) * kTokTile;
-  int2 *to = flags + static_cast<size_t>(bh) * n + pre;
-  for (int j = lane; j < c; j += 64) to[j] = from[j];
-  if (t == tph - 1 && lane == 0) qcount[bh] = pre + c;
+  if (lane == 0) s_part[wave] = pre;
+  __syncthreads();
+  if (wave == 0) {
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) base += s_part[w];
+    const int c = t0 + lane < tph ? cnt[t0 + lane] : 0;
+    int v = c;   // inclusive scan over the 64 lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(v, o);
+      if (lane >= o) v += y;
+    }
+    s_off[lane] = base + v - c;
+    if (lane == 63) s_off[kJoinTiles] = base + v;
+  }
+  __syncthreads();
+  // the block's rows in output order: row e belongs to the last tile j with
+  // s_off[j] <= e (binary search; tiles past the slice end are empty)
+  const int first = s_off[0], total = s_off[kJoinTiles] - first;
+  const int2 *from = tflags + static_cast<size_t>(bh) * n + static_cast<size_t>(t0) * rt;
+  int2 *to = flags + static_cast<size_t>(bh) * n + first;
+  for (int e = tid; e < total; e += kThreads) {
+    int lo = 0;
+#pragma unroll
+    for (int step = kJoinTiles / 2; step > 0; step >>= 1)
+      if (s_off[lo + step] - first <= e) lo += step;
+    to[e] = from[static_cast<size_t>(lo) * rt + (e - (s_off[lo] - first))];
+  }
+  if (t0 + kJoinTiles >= tph && tid == 0) qcount[bh] = s_off[kJoinTiles];
 }
 
 // ---------------------------------------------------------------------------
@@ -860,6 +1128,18 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e; \
   } while (0)
 
+  // up to kResTiles centroid tiles: the resident-table main pass, one
+  // workgroup per compute unit (at least one per slice), 64-token tiles
+  const bool resident = cpad <= kResTiles * 32;
+  const int rtph = (a.n + kResTok - 1) / kResTok;
+  const long long rtiles = static_cast<long long>(a.bh) * rtph;
+  const int rgrid = static_cast<int>(std::max<long long>(
+      a.bh, std::min<long long>(device_cus(), (rtiles + kResWaves - 1) / kResWaves)));
+#define SVA_RES(NTL)                                                                          \
+  hipLaunchKernelGGL((km_assign_res_kernel<D, NTL>), dim3(rgrid), dim3(64 * kResWaves), 0, s, \
+                     static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,        \
+                     a.assign, tflags, tcount, a.bh, rtph)
+
   // clusters of 256 rows or more on average get four waves each
   const bool wide = a.n >= 256LL * a.c;
   auto mean = [&](int mode) -> hipError_t {
@@ -890,7 +1170,14 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
       // the pair path (third best tracked) pays once the refine's re-scan is
       // long: with 8 or more centroid tiles
       const bool pairs = cpad >= 8 * 32;
-      if (pairs)
+      if (resident) {
+        switch (cpad / 32) {
+          case 1: SVA_RES(1); break;
+          case 2: SVA_RES(2); break;
+          case 3: SVA_RES(3); break;
+          default: SVA_RES(4); break;
+        }
+      } else if (pairs)
         hipLaunchKernelGGL((km_assign_main_kernel<D, true>), tok_grid, dim3(kThreads), 0, s,
                            static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
                            a.assign, tflags, tcount, pcount, a.bh, tph);
@@ -904,8 +1191,10 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
                            static_cast<const uint16_t *>(a.x), a.n, a.c, a.centroids, tflags,
                            pcount, a.assign, a.n_refined, a.bh, tph);
       SVA_CHECK(hipGetLastError());
-      hipLaunchKernelGGL(km_queue_join_kernel, dim3((tph + kThreads / 64 - 1) / (kThreads / 64), a.bh),
-                         dim3(kThreads), 0, s, tflags, tcount, a.n, tph, flags, ctl);
+      const int jt = resident ? rtph : tph;
+      hipLaunchKernelGGL(km_queue_join_kernel, dim3((jt + kJoinTiles - 1) / kJoinTiles, a.bh),
+                         dim3(kThreads), 0, s, tflags, tcount, a.n, jt,
+                         resident ? kResTok : kTokTile, flags, ctl);
       SVA_CHECK(hipGetLastError());
       hipLaunchKernelGGL((km_refine_kernel<D>), tok_grid, dim3(kThreads), 0, s,
                          static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, ctl,
@@ -923,6 +1212,7 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     SVA_CHECK(mean((bf16 && !last) ? 1 : 2));
   }
 #undef SVA_CHECK
+#undef SVA_RES
   return hipSuccess;
 }
 

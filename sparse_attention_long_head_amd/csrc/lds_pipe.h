@@ -66,6 +66,41 @@ __device__ __forceinline__ void lds_read_frags(bf16x8 (&f)[N], const uint32_t (&
   }
 }
 
+// Row fragments at one lane address: N = 4 or 8 ds_read_b128 at a + OFF + STRIDE * s.
+template <int OFF, int STRIDE, int N>
+__device__ __forceinline__ void lds_read_frags_strided(bf16x8 (&f)[N], uint32_t a) {
+  static_assert(OFF >= 0 && OFF + (N - 1) * STRIDE < 65536, "ds offset field");
+  if constexpr (N == 8) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%9\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %8 offset:%14\n\t"
+        "ds_read_b128 %6, %8 offset:%15\n\t"
+        "ds_read_b128 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+          "=&v"(f[6]), "=&v"(f[7])
+        : "v"(a), "i"(OFF), "i"(OFF + STRIDE), "i"(OFF + 2 * STRIDE), "i"(OFF + 3 * STRIDE),
+          "i"(OFF + 4 * STRIDE), "i"(OFF + 5 * STRIDE), "i"(OFF + 6 * STRIDE),
+          "i"(OFF + 7 * STRIDE)
+        : "memory");
+  } else {
+    static_assert(N == 4, "4 or 8 fragments");
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(a), "i"(OFF), "i"(OFF + STRIDE), "i"(OFF + 2 * STRIDE), "i"(OFF + 3 * STRIDE)
+        : "memory");
+  }
+}
+
 // Transposed fragments: for each of N d tiles two ds_read_b64_tr_b16 (rows +0
 // and +HI of the k-step) joined into one 8-element operand.
 template <int OFF, int HI, int N>

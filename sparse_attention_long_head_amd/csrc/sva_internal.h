@@ -118,6 +118,9 @@ hipError_t launch_block_means(const void *x, int32_t dtype, int32_t bh, int32_t 
 
 hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t s);
 
+// compute units of the current device (persistent grids); 256 if the query fails
+int device_cus();
+
 constexpr int kMaxClustersSort = 16384;   // LDS counter capacity of the sort
 constexpr int kMaxSelectK = 4096;         // LDS sort capacity of top-p selection
 

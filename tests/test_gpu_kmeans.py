@@ -52,12 +52,22 @@ def test_tiny_config_lockstep_fp32():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("c", [1, 37, 300])
+@pytest.mark.parametrize("c", [1, 37, 90, 128, 300])
 def test_small_video_lockstep_bf16(d, c):
     cfg = synth.CONFIGS["5s"].with_(T=3, heads=2, d=d)      # 4,680 tokens, ragged tile tail
     x = synth.video_qkv(cfg)["k"]
     init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "k", c))
     ties, refined = _lockstep(x, init, c, 4, torch.bfloat16)
+    assert ties <= 2
+
+
+def test_many_slices_few_tokens():
+    """More slices than compute units with one 64-token tile each (ragged):
+    one workgroup per slice in the resident-table pass."""
+    cfg = synth.CONFIGS["5s"].with_(T=1, H=6, W=13, heads=300, d=64)   # 78 tokens
+    x = synth.video_qkv(cfg)["q"]
+    init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "q", 20))
+    ties, _ = _lockstep(x, init, 20, 2, torch.bfloat16)
     assert ties <= 2
 
 
