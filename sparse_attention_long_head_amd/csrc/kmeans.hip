@@ -8,11 +8,17 @@
 //   w_c = x.c - ||c||^2 / 2.  The dot products run on 32x32x16 bf16 MFMA with
 //   clusters on the accumulator rows and tokens on lanes; the accumulator
 //   starts at -||c||^2/2, so no VALU op is spent on it.  x is exactly bf16 and
-//   every fp32 centroid is split into bf16 hi + lo (residual <= 2^-16 |c|).
+//   every fp32 centroid is split into bf16 hi + lo: hi and lo are
+//   round-to-nearest conversions and c - hi is exact in fp32, so each element's
+//   residual is at most 2^-18 of it.
 //   Each lane keeps the three best w of its clusters (max + two med3) and the
 //   tiles of the best two; the two lane halves merge.  Every w carries a rigorous
 //   error bound E (split residual + fp32 accumulation of 2d exact products and
-//   the start value + final rounding, from ||x|| and max ||c||).  A row whose
+//   the start value + final rounding, from ||x|| and max ||c||).  Additions
+//   inside and between the MFMAs round to nearest even (checked on the GPU:
+//   ties go to even and partial sums can round up, which no truncating adder
+//   does), so each contributes at most 2^-24 of its operands' magnitude,
+//   whatever the order in which an MFMA adds its products.  A row whose
 //   best two w are more than 2E apart is decided.  A row whose third-best w
 //   is more than 2E below its best has exactly two candidates (no other
 //   cluster can be the argmin): it goes to the pair list of its token tile
@@ -21,7 +27,7 @@
 //   of a region of its own and its pairs to the back; a join kernel
 //   concatenates the queue parts in tile order, so there are no atomics and
 //   the queue order is deterministic).
-// pair: one thread per listed row computes the exact fp64 distances to its two
+// pair: d/8 lanes per listed row compute the exact fp64 distances to its two
 //   candidates; the smaller wins, ties to the lower index.
 // refine: queued rows run through the same MFMA loop; every cluster with
 //   w >= threshold (a set that provably holds the true argmin) goes to an LDS
@@ -312,8 +318,8 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
   const bool pairs_ok = PAIRS && c <= 65536;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx[nt] * cm +
-                    (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx[nt] * cm) +
+    const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx[nt] * cm +
+                    (2.f * D) * 0x1p-24f * (0.5f * cm * cm + 1.02f * nx[nt] * cm) +
                     0x1p-19f * (nx[nt] * cm + 0.5f * cm * cm);
     const float two_e = 2.f * 1.25f * e;
     const int i1 = t1[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
@@ -567,8 +573,8 @@ __global__ __launch_bounds__(64 * kResWaves, 1) void km_assign_res_kernel(
         }
       p += xor32(p);
       const float nx = sqrtf(p) * (1.f + 0x1p-10f) + 0x1p-60f;
-      const float e = 0x1p-25f * cm * cm + 0x1p-16f * nx * cm +
-                      (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx * cm) +
+      const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx * cm +
+                      (2.f * D) * 0x1p-24f * (0.5f * cm * cm + 1.02f * nx * cm) +
                       0x1p-19f * (nx * cm + 0.5f * cm * cm);
       const float two_e = 2.f * 1.25f * e;
       const int i1 = t1r[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
