@@ -1174,8 +1174,8 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     const bool last = it + 1 == a.iters;
     if (bf16) {
       // the pair path (third best tracked) pays once the refine's re-scan is
-      // long: with 8 or more centroid tiles
-      const bool pairs = cpad >= 8 * 32;
+      // long: with more than 32 centroid tiles (measured break-even near 32)
+      const bool pairs = cpad > 32 * 32;
       if (resident) {
         switch (cpad / 32) {
           case 1: SVA_RES(1); break;

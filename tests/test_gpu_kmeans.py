@@ -52,7 +52,7 @@ def test_tiny_config_lockstep_fp32():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("c", [1, 37, 90, 128, 300])
+@pytest.mark.parametrize("c", [1, 37, 90, 128, 300, 1100])
 def test_small_video_lockstep_bf16(d, c):
     cfg = synth.CONFIGS["5s"].with_(T=3, heads=2, d=d)      # 4,680 tokens, ragged tile tail
     x = synth.video_qkv(cfg)["k"]
@@ -72,14 +72,14 @@ def test_many_slices_few_tokens():
 
 
 def test_pair_path_with_duplicate_centroids():
-    # 300 clusters (10 centroid tiles: the two-candidate path is on) with one
+    # 1,100 clusters (35 centroid tiles: the two-candidate path is on) with one
     # centroid doubled and one tripled, in different tiles and at the same row
     # of a tile (bit-equal w with equal row bits): rows nearest a doubled
     # centroid are two-candidate rows that tie exactly (the lower id wins),
     # rows nearest the tripled one have three candidates (refine pass)
     cfg = synth.CONFIGS["5s"].with_(T=2, heads=2)             # 3,120 tokens
     x = synth.video_qkv(cfg)["k"]
-    c = 300
+    c = 1100
     init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "k", c)).copy()
     for h in range(2):
         init[0, h, 32 + 7] = init[0, h, 7]                    # same row of tiles 0 and 1
