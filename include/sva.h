@@ -283,6 +283,22 @@ int32_t sva_full_attn(const void *q, const void *k, const void *v, int32_t dtype
                       int32_t heads, int32_t n_q, int32_t n_k, int32_t d, float scale, void *o,
                       int32_t o_dtype, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * sva_check_mfma_rounding -- checks on the current GPU the model of the
+ * hardware that sva_kmeans's error bound assumes: the 32x32x16 bf16
+ * matrix-multiply instruction accumulates its products and the value it is
+ * seeded with in fp32 (24-bit significand), each addition losing at most one
+ * unit in the last place, in any order.  Eight cases with known answers:
+ * four whose every partial sum is exact in fp32 (they must come out exact)
+ * and four that need rounding (they must land within one unit per addition).
+ *
+ *   flags   [8] int32 device memory, OUT: 1 where the case meets the model,
+ *           0 otherwise.  The caller owns it.
+ * Returns SVA_EINVAL for a NULL flags, SVA_EHIP if the launch fails;
+ * asynchronous on stream like the other calls.
+ * ------------------------------------------------------------------------ */
+int32_t sva_check_mfma_rounding(int32_t *flags, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

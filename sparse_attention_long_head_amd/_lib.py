@@ -49,6 +49,7 @@ SIGNATURES = {
     "sva_unpermute": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "sva_full_attn_workspace_bytes": (_Z, [_I, _I, _I]),
     "sva_full_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _Z, _P]),
+    "sva_check_mfma_rounding": (_I, [_P, _P]),
 }
 
 _lib = None
@@ -290,6 +291,16 @@ def sva_block_sparse_attn_perm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         kept_idx.shape[-1], float(scale), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(w), wb,
         _stream(q)), "sva_block_sparse_attn_perm")
     return o, lse
+
+
+def sva_check_mfma_rounding(device=None) -> list:
+    """Flags (8 ints) of the on-device accumulation check; all 1 on hardware
+    whose bf16 MFMA accumulates with a 24-bit significand, at most one unit
+    in the last place lost per addition (the k-means error bound's model)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    flags = torch.full((8,), -1, dtype=torch.int32, device=dev)
+    _check(lib().sva_check_mfma_rounding(_ptr(flags), _stream(flags)), "sva_check_mfma_rounding")
+    return flags.cpu().tolist()
 
 
 def sva_unpermute(o_perm: torch.Tensor, perm: torch.Tensor, o: Optional[torch.Tensor] = None):

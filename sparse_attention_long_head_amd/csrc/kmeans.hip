@@ -14,11 +14,13 @@
 //   Each lane keeps the three best w of its clusters (max + two med3) and the
 //   tiles of the best two; the two lane halves merge.  Every w carries a rigorous
 //   error bound E (split residual + fp32 accumulation of 2d exact products and
-//   the start value + final rounding, from ||x|| and max ||c||).  Additions
-//   inside and between the MFMAs round to nearest even (checked on the GPU:
-//   ties go to even and partial sums can round up, which no truncating adder
-//   does), so each contributes at most 2^-24 of its operands' magnitude,
-//   whatever the order in which an MFMA adds its products.  A row whose
+//   the start value + final rounding, from ||x|| and max ||c||).  Each
+//   addition inside and between the MFMAs is taken to lose at most one unit
+//   in the last place of fp32 (2^-23 of its operands' magnitude) in any
+//   order: the seed's addition rounds to nearest even, but the additions
+//   among an MFMA's products do not (-2^25 + 2^25 + 3 gives 2), so no
+//   round-to-nearest half-unit is assumed.  sva_check_mfma_rounding checks
+//   this model on the device.  A row whose
 //   best two w are more than 2E apart is decided.  A row whose third-best w
 //   is more than 2E below its best has exactly two candidates (no other
 //   cluster can be the argmin): it goes to the pair list of its token tile
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx[nt] * cm +
-                    (2.f * D) * 0x1p-24f * (0.5f * cm * cm + 1.02f * nx[nt] * cm) +
+                    (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx[nt] * cm) +
                     0x1p-19f * (nx[nt] * cm + 0.5f * cm * cm);
     const float two_e = 2.f * 1.25f * e;
     const int i1 = t1[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(64 * kResWaves, 1) void km_assign_res_kernel(
       p += xor32(p);
       const float nx = sqrtf(p) * (1.f + 0x1p-10f) + 0x1p-60f;
       const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx * cm +
-                      (2.f * D) * 0x1p-24f * (0.5f * cm * cm + 1.02f * nx * cm) +
+                      (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx * cm) +
                       0x1p-19f * (nx * cm + 0.5f * cm * cm);
       const float two_e = 2.f * 1.25f * e;
       const int i1 = t1r[nt] * 32 + acc_row(__float_as_int(b1[nt]) & 15, h);
@@ -1174,8 +1176,8 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     const bool last = it + 1 == a.iters;
     if (bf16) {
       // the pair path (third best tracked) pays once the refine's re-scan is
-      // long: with more than 32 centroid tiles (measured break-even near 32)
-      const bool pairs = cpad > 32 * 32;
+      // long: with 16 or more centroid tiles (measured break-even between 13 and 16)
+      const bool pairs = cpad >= 16 * 32;
       if (resident) {
         switch (cpad / 32) {
           case 1: SVA_RES(1); break;
@@ -1223,6 +1225,62 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// The arithmetic the assign pass's error bound relies on: the 32x32x16 bf16
+// MFMA accumulates with a 24-bit significand and each addition loses at most
+// one unit in the last place.  One wave evaluates D = C + A.B with B all
+// ones, so row r of D is C[r] + the sum of row r of A (products at k = 0, 5,
+// 11).  Cases 0-3 have every partial sum exact in fp32, in any order, so
+// they must come out exact; cases 4-7 need rounding and must land within one
+// unit per addition of the exact value (both round-to-nearest and
+// truncating results pass).  Case r's flag is 1 when it holds.
+// ---------------------------------------------------------------------------
+namespace {
+__global__ __launch_bounds__(64) void km_mfma_rounding_kernel(int32_t *__restrict__ flags) {
+  const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
+  const float p23 = 0x1p23f, p24 = 0x1p24f, p25 = 0x1p25f;
+  // per case: the seed C, three products (A entries), the exact result and
+  // the allowed error (one unit in the last place per addition: 2 below 2^25,
+  // 4 below 2^26; three additions)
+  const float seed[kMfmaChecks] = {0.f, p23, -p23, 0.f, p24 + 2.f, p24, -p25, 0.f};
+  const float prod[kMfmaChecks][3] = {{p23, 1.f, -p23}, {1.f, -p23, 0.f}, {p23, 1.f, 0.f},
+                                      {1.f, p23, -p23}, {1.f, 0.f, 0.f},  {1.f, 1.f, 0.f},
+                                      {p25, 3.f, 0.f},  {p25, 3.f, -p25}};
+  const float exact[kMfmaChecks] = {1.f, 1.f, 1.f, 1.f, p24 + 3.f, p24 + 2.f, 3.f, 3.f};
+  const float tol[kMfmaChecks] = {0.f, 0.f, 0.f, 0.f, 2.f * 3.f, 2.f * 3.f, 4.f * 3.f, 4.f * 3.f};
+  // A fragment of this lane: row col, k = 8h .. 8h+7 (products in k = 0, 5, 11)
+  bf16x8 a;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = 8 * h + j;
+    const float v = col < kMfmaChecks ? (k == 0 ? prod[col][0] : k == 5 ? prod[col][1]
+                                         : k == 11 ? prod[col][2] : 0.f) : 0.f;
+    a[j] = static_cast<__bf16>(v);   // every product above is exact in bf16
+  }
+  bf16x8 b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = static_cast<__bf16>(1.f);
+  f32x16 c;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = acc_row(i, h);
+    c[i] = row < kMfmaChecks ? seed[row] : 0.f;
+  }
+  const f32x16 d = mfma32x32x16(a, b, c);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = acc_row(i, h);
+    if (col == 0 && row < kMfmaChecks)
+      flags[row] = fabsf(d[i] - exact[row]) <= tol[row] ? 1 : 0;
+  }
+}
+}  // namespace
+
+hipError_t launch_mfma_rounding_check(int32_t *flags, hipStream_t s) {
+  hipLaunchKernelGGL(km_mfma_rounding_kernel, dim3(1), dim3(64), 0, s, flags);
+  return hipGetLastError();
+}
 
 size_t kmeans_ws_bytes(int32_t bh, int32_t n, int32_t d, int32_t c) {
   return km_layout(bh, n, d, c).total;

@@ -309,6 +309,13 @@ int32_t sva_full_attn(const void *q, const void *k, const void *v, int32_t dtype
 }
 
 // ---------------------------------------------------------------------------
+int32_t sva_check_mfma_rounding(int32_t *flags, void *stream) {
+  const char *fn = "sva_check_mfma_rounding";
+  if (!flags) return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  return hip_status(sva::launch_mfma_rounding_check(flags, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
 int32_t sva_unpermute(const void *o_perm, const int32_t *perm, int32_t dtype, int32_t batch,
                       int32_t heads, int32_t n, int32_t d, void *o, void *stream) {
   const char *fn = "sva_unpermute";

@@ -121,6 +121,10 @@ hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t 
 // compute units of the current device (persistent grids); 256 if the query fails
 int device_cus();
 
+// the accumulate-path rounding check of the bf16 MFMA (flags[kMfmaChecks])
+constexpr int kMfmaChecks = 8;
+hipError_t launch_mfma_rounding_check(int32_t *flags, hipStream_t s);
+
 constexpr int kMaxClustersSort = 16384;   // LDS counter capacity of the sort
 constexpr int kMaxSelectK = 4096;         // LDS sort capacity of top-p selection
 

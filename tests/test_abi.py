@@ -42,6 +42,11 @@ def test_exports_every_declared_symbol(L):
 P = ctypes.c_void_p(256)   # a non-NULL dummy: nothing may be dereferenced before validation
 
 
+def test_rounding_check_validation(L):
+    assert L.lib().sva_check_mfma_rounding(None, None) == 1   # SVA_EINVAL, nothing launched
+    assert "NULL" in L.last_error()
+
+
 def test_kmeans_validation(L):
     lib = L.lib()
     ws = lib.sva_kmeans_workspace_bytes(1, 2, 1000, 128, 10)

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from parity import TIE, assign_parity, device, host, to_dev
-from sparse_attention_long_head_amd import sva_kmeans
+from sparse_attention_long_head_amd import sva_check_mfma_rounding, sva_kmeans
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,13 @@ def test_small_video_lockstep_bf16(d, c):
     init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "k", c))
     ties, refined = _lockstep(x, init, c, 4, torch.bfloat16)
     assert ties <= 2
+
+
+def test_mfma_accumulation_model():
+    """The hardware model the k-means error bound assumes: the bf16 MFMA
+    accumulates in fp32 and loses at most one unit in the last place per
+    addition (2^-23), whatever the order of its additions."""
+    assert sva_check_mfma_rounding() == [1] * 8
 
 
 def test_many_slices_few_tokens():
