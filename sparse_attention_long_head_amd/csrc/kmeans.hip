@@ -209,20 +209,24 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
   for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
   if (lane == 0) s_nhmin[wave] = mn;
 
-  // ||x|| bound per token
+  // ||x|| bound per token: bf16 pair dot products (exact products, fp32
+  // sums); the 2^-60 covers products below the fp32 normal range if flushed
   float nx[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float p = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2)
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const u32x4 u = __builtin_bit_cast(u32x4, xf[nt][s2]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float f = static_cast<float>(xf[nt][s2][j]);
-        p = fmaf(f, f, p);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = u[j];
+        const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+        p = __builtin_amdgcn_fdot2_f32_bf16(v, v, p, false);
       }
+    }
     p += __shfl_xor(p, 32);
-    nx[nt] = sqrtf(p) * (1.f + 0x1p-10f);
+    nx[nt] = sqrtf(p) * (1.f + 0x1p-10f) + 0x1p-60f;
   }
 
   // LDS byte addresses of this lane's A fragments (centroid row col, piece
