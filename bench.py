@@ -118,9 +118,9 @@ def main() -> int:
                          "335.5 MB written at 5 s) to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every stage is independent per head; see the sharding notes in the design "
-              "document).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the path runs on a single GPU (every stage "
+              "is independent per head, so heads would shard across GPUs with no exchange).  "
+              "Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch

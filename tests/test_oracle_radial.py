@@ -3,7 +3,7 @@ dynamic-threshold selection in the oracle (CPU only).
 
 * closed-form candidate counts for an interior block of a frame-aligned grid;
 * the 5 s clip geometry's radial density 0.1296 and per-row counts 15 / 33.2 / 41
-  (established independently when the workload was surveyed);
+  (figures recorded for the full-size geometry, kept as a regression pin);
 * symmetry, the diagonal, ratio 1 = the candidate set, ratio 0 = nothing,
   monotonicity in the ratios, ceil(r * n) kept per distance and nearest first;
 * block means of an arithmetic ramp in closed form;
