@@ -78,6 +78,18 @@ def test_many_slices_few_tokens():
     assert ties <= 2
 
 
+@pytest.mark.parametrize("w,d", [(5, 128), (64, 64), (65, 128), (128, 128)])
+def test_resident_pass_tile_edges(w, d):
+    """Slices of fewer than one 64-token tile, exactly one or two tiles, and one
+    token past a tile (the resident-table pass, C <= 128)."""
+    cfg = synth.CONFIGS["5s"].with_(T=1, H=1, W=w, heads=5, d=d)
+    x = synth.video_qkv(cfg)["q"]
+    c = min(3, w)
+    init = synth.gather_init(x, synth.kmeans_init_indices(cfg, "q", c))
+    ties, _ = _lockstep(x, init, c, 2, torch.bfloat16)
+    assert ties == 0
+
+
 def test_pair_path_with_duplicate_centroids():
     # 1,100 clusters (35 centroid tiles: the two-candidate path is on) with one
     # centroid doubled and one tripled, in different tiles and at the same row
