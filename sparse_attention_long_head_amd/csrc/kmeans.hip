@@ -71,7 +71,7 @@ __device__ __forceinline__ int cswz(int r) {
 }
 
 struct KmLayout {
-  size_t chi, clo, nh, ctl, flags, tflags, tcount, pcount, perm, offsets, order, sort, total;
+  size_t chi, clo, nh, ctl, flags, tflags, tcount, pcount, perm, offsets, sort, total;
 };
 
 // ctl holds the bh refine-queue lengths
@@ -94,7 +94,6 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   L.pcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
   L.perm = take(static_cast<size_t>(bh) * n * 4);
   L.offsets = take(static_cast<size_t>(bh) * (c + 1) * 4);
-  L.order = take(static_cast<size_t>(bh) * cpad * 4);
   L.sort = take(sort_ws_bytes(bh, n, c));
   L.total = off;
   return L;
@@ -995,9 +994,8 @@ constexpr int kMeanWaves = 4;
 template <int D, bool BF16, int WPC>
 __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
     const void *__restrict__ x, int n, int c, int cpad, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ order,
-    float *__restrict__ cent, uint16_t *__restrict__ chi, uint16_t *__restrict__ clo,
-    float *__restrict__ nh, int mode, int ncl) {
+    const int32_t *__restrict__ offsets, float *__restrict__ cent, uint16_t *__restrict__ chi,
+    uint16_t *__restrict__ clo, float *__restrict__ nh, int mode, int ncl) {
   constexpr int EB = BF16 ? 2 : 4;           // element bytes
   constexpr int EPT = 16 / EB;               // elements per 16-byte piece
   constexpr int TPR = D / EPT;               // lanes per row
@@ -1008,15 +1006,11 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
   __shared__ double s_part[WPC > 1 ? WPC : 1][WPC > 1 ? D : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wc = WPC > 1 ? wave : 0;         // this wave's rank within its cluster
-  // with an order (after a sort): the grid is (slice, rank), launched rank
-  // by rank across slices, and rank r of a slice is its r-th largest cluster,
-  // so the longest clusters start first.  Without (the initial prep): (cluster,
-  // slice), slices in reverse launch order.
-  const int slot = order != nullptr ? blockIdx.y : blockIdx.x;
-  const int r = WPC > 1 ? slot : slot * kMeanWaves + wave;
-  const int bh = order != nullptr ? blockIdx.x : gridDim.y - 1 - blockIdx.y;
-  if (r >= ncl) return;                      // uniform over the cluster's waves
-  const int cl = order != nullptr ? order[static_cast<size_t>(bh) * cpad + r] : r;
+  // slices in reverse launch order: the assign pass just before walked them in
+  // ascending order, so the last ones it read are the likeliest still cached
+  const int cl = WPC > 1 ? blockIdx.x : blockIdx.x * kMeanWaves + wave;
+  const int bh = gridDim.y - 1 - blockIdx.y;
+  if (cl >= ncl) return;                     // uniform over the cluster's waves
   const bool real = cl < c;
   const int g = lane / TPR, pc = lane % TPR;
   float val[EPT];                            // coordinates pc*EPT.. of the final centroid
@@ -1160,16 +1154,13 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
 
   // clusters of 256 rows or more on average get four waves each
   const bool wide = a.n >= 256LL * a.c;
-  int32_t *order = reinterpret_cast<int32_t *>(w + L.order);
   auto mean = [&](int mode) -> hipError_t {
     const int ncl = mode == 2 ? a.c : cpad;
-    const int slots = wide ? ncl : (ncl + kMeanWaves - 1) / kMeanWaves;
-    const int32_t *ord = mode == 0 ? nullptr : order;   // the order comes from the sort
-    const dim3 grid = ord != nullptr ? dim3(a.bh, slots) : dim3(slots, a.bh);
+    const dim3 grid(wide ? ncl : (ncl + kMeanWaves - 1) / kMeanWaves, a.bh);
     const dim3 block(64 * kMeanWaves);
 #define SVA_MEAN(B, W)                                                                       \
   hipLaunchKernelGGL((km_mean_kernel<D, B, W>), grid, block, 0, s, a.x, a.n, a.c, cpad, perm, \
-                     offsets, ord, a.centroids, chi, clo, nh, mode, ncl)
+                     offsets, a.centroids, chi, clo, nh, mode, ncl)
     if (bf16) {
       if (wide) SVA_MEAN(true, kMeanWaves);
       else SVA_MEAN(true, 1);
@@ -1229,8 +1220,7 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     }
     // the sort's scan clears the per-slice queue lengths for the next iteration
     SVA_CHECK(launch_cluster_sort(a.assign, a.bh, a.n, a.c, perm, offsets,
-                                  last ? a.sizes : nullptr, sort_ws, s, bf16 ? ctl : nullptr,
-                                  order, cpad));
+                                  last ? a.sizes : nullptr, sort_ws, s, bf16 ? ctl : nullptr));
     SVA_CHECK(mean((bf16 && !last) ? 1 : 2));
   }
 #undef SVA_CHECK

@@ -90,20 +90,11 @@ __global__ __launch_bounds__(kThreads) void sort_scan_rows_kernel(
 
 // per slice: offsets[0, c) holds the cluster sizes; replaced in place by their
 // exclusive scan (4 consecutive clusters per thread per round), offsets[c] = n
-// order (optional, [bh][cpad]): the slice's clusters largest first, bucketed
-// by the bit length of their size (order within a bucket is unspecified),
-// then the padding ids c .. cpad-1; a schedule for per-cluster work
 __global__ __launch_bounds__(kScanThreads) void sort_scan_totals_kernel(
     int n, int c, int32_t *__restrict__ offsets, int32_t *__restrict__ sizes,
-    int32_t *__restrict__ clear, int32_t *__restrict__ order, int cpad) {
-  constexpr int kBuckets = 33;
+    int32_t *__restrict__ clear) {
   __shared__ int32_t wsum[kScanThreads / 64];
-  __shared__ int32_t s_cnt[kBuckets], s_cur[kBuckets];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kBuckets) {
-    s_cnt[tid] = 0;
-    s_cur[tid] = 0;
-  }
   int32_t *off = offsets + static_cast<size_t>(bh) * (c + 1);
   int32_t *sz = sizes != nullptr ? sizes + static_cast<size_t>(bh) * c : nullptr;
   int carry = 0;
@@ -142,29 +133,6 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_totals_kernel(
     off[c] = n;
     if (clear != nullptr) clear[bh] = 0;   // a per-slice counter of the caller
   }
-  if (order == nullptr) return;   // uniform
-  __syncthreads();
-  auto bucket = [&](int cl) {
-    const int s = off[cl + 1] - off[cl];
-    return s == 0 ? 0 : 32 - __clz(s);
-  };
-  for (int cl = tid; cl < c; cl += kScanThreads) atomicAdd(&s_cnt[bucket(cl)], 1);
-  __syncthreads();
-  if (tid == 0) {   // bucket starts, largest sizes first
-    int acc = 0;
-    for (int b = kBuckets - 1; b >= 0; --b) {
-      const int k = s_cnt[b];
-      s_cnt[b] = acc;
-      acc += k;
-    }
-  }
-  __syncthreads();
-  int32_t *ord = order + static_cast<size_t>(bh) * cpad;
-  for (int cl = tid; cl < c; cl += kScanThreads) {
-    const int b = bucket(cl);
-    ord[s_cnt[b] + atomicAdd(&s_cur[b], 1)] = cl;
-  }
-  for (int cl = c + tid; cl < cpad; cl += kScanThreads) ord[cl] = cl;
 }
 
 __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
@@ -221,7 +189,7 @@ size_t sort_ws_bytes(int32_t bh, int32_t n, int32_t c) {
 
 hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int32_t c,
                                int32_t *perm, int32_t *offsets, int32_t *sizes, void *ws,
-                               hipStream_t s, int32_t *clear, int32_t *order, int32_t cpad) {
+                               hipStream_t s, int32_t *clear) {
   const int tiles = (n + kTile - 1) / kTile;
   const size_t hist_bytes = align_up(static_cast<size_t>(bh) * c * tiles * 4, 256);
   int32_t *hist = static_cast<int32_t *>(ws);
@@ -236,7 +204,7 @@ hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sort_scan_totals_kernel, dim3(bh), dim3(kScanThreads), 0, s, n, c, offsets,
-                     sizes, clear, order, cpad);
+                     sizes, clear);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3((n + kThreads - 1) / kThreads, bh),

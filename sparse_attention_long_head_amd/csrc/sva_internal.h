@@ -76,14 +76,11 @@ size_t kmeans_ws_bytes(int32_t bh, int32_t n, int32_t d, int32_t c);
 hipError_t launch_kmeans(const KmeansArgs &a, hipStream_t s);
 
 // stable counting sort of rows by cluster id (shared by k-means and permute);
-// `clear`, if not NULL, holds bh ints that the sort sets to zero; `order`, if
-// not NULL, [bh][cpad] receives each slice's clusters largest first (padding
-// ids c .. cpad-1 last)
+// `clear`, if not NULL, holds bh ints that the sort sets to zero
 size_t sort_ws_bytes(int32_t bh, int32_t n, int32_t c);
 hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int32_t c,
                                int32_t *perm, int32_t *offsets, int32_t *sizes, void *ws,
-                               hipStream_t s, int32_t *clear = nullptr,
-                               int32_t *order = nullptr, int32_t cpad = 0);
+                               hipStream_t s, int32_t *clear = nullptr);
 hipError_t launch_gather_rows(const void *src, void *dst, const int32_t *perm, int32_t bh,
                               int32_t n, int32_t row_bytes, int32_t scatter, hipStream_t s);
 
