@@ -79,9 +79,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const float *__restrict__ cent_k, const int32_t *__restrict__ size_k, int cq, int ck, int ckp,
     double scale, double top_p, uint8_t *__restrict__ mask, int32_t *__restrict__ kept_count,
     int32_t *__restrict__ kept_idx) {
-  __shared__ double key[kCap];
-  __shared__ int32_t idx[kCap];
-  __shared__ uint8_t mk[kCap];
+  // sort arrays sized by the launch for ckp keys (not the kCap maximum), so
+  // small C_k leaves room for more workgroups per CU
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_sel[];
+  double *key = reinterpret_cast<double *>(s_sel);              // [ckp]
+  int32_t *idx = reinterpret_cast<int32_t *>(key + ckp);         // [ckp]
+  uint8_t *mk = reinterpret_cast<uint8_t *>(idx + ckp);          // [ck]
   __shared__ double sq[D];
   __shared__ double red[kThreads / 64];
   __shared__ int ired[kThreads / 64];
@@ -332,11 +335,12 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   int ckp = 1;
   while (ckp < a.ck) ckp <<= 1;
   const dim3 grid(a.cq, a.bh);
+  const size_t lds = static_cast<size_t>(ckp) * (8 + 4) + align_up(static_cast<size_t>(a.ck), 16);
   if (a.d == 128)
-    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kThreads), 0, s, a.cent_q, a.size_q,
+    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kThreads), lds, s, a.cent_q, a.size_q,
                        a.cent_k, a.size_k, a.cq, a.ck, ckp, a.scale, a.top_p, a.mask, a.kept_count, a.kept_idx);
   else
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), 0, s, a.cent_q, a.size_q,
+    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), lds, s, a.cent_q, a.size_q,
                        a.cent_k, a.size_k, a.cq, a.ck, ckp, a.scale, a.top_p, a.mask, a.kept_count, a.kept_idx);
   return hipGetLastError();
 }
