@@ -134,3 +134,51 @@ def test_row_sample_is_exact():
     # equal up to BLAS blocking (one ulp)
     np.testing.assert_allclose(o2, o[rows], rtol=0, atol=1e-13)
     np.testing.assert_allclose(lse2, lse[rows], rtol=0, atol=1e-13)
+
+
+def _brute_block_sparse(q, k, v, mask, block, scale):
+    """Per-element loops with math.fsum: query row r sees key j iff
+    mask[r // block][j // block]; a row that sees no key gets O = 0, LSE = -inf."""
+    nq, d = q.shape
+    o = np.zeros((nq, v.shape[1]))
+    lse = np.full(nq, -np.inf)
+    for r in range(nq):
+        allowed = [j for j in range(k.shape[0]) if mask[r // block][j // block]]
+        if not allowed:
+            continue
+        logits = [scale * math.fsum(q[r, t] * k[j, t] for t in range(d)) for j in allowed]
+        mx = max(logits)
+        ex = [math.exp(s - mx) for s in logits]
+        den = math.fsum(ex)
+        for t in range(v.shape[1]):
+            o[r, t] = math.fsum(e * v[j, t] for e, j in zip(ex, allowed)) / den
+        lse[r] = mx + math.log(den)
+    return o, lse
+
+
+@pytest.mark.parametrize("nq,nk,block,seed", [(11, 11, 4, 0), (37, 45, 8, 1), (9, 30, 4, 2)])
+def test_block_sparse_matches_brute_force(nq, nk, block, seed):
+    """Uniform-block masked attention (DynamicRad explainer, technical summary
+    section 2.a: a fixed block mask) on asymmetric masks with ragged last blocks,
+    different query and key lengths and a query block that keeps nothing: a
+    transposed mask, keys taken from the query's block, or a dropped ragged tail
+    all fail here."""
+    rng = np.random.default_rng(40 + seed)
+    d = 5
+    q, k, v = (rng.standard_normal((n, d)) for n in (nq, nk, nk))
+    nqb, nkb = -(-nq // block), -(-nk // block)
+    if (nq, nk) == (11, 11):
+        mask = np.array([[1, 1, 0], [0, 0, 0], [1, 0, 1]], bool)
+    else:
+        mask = rng.random((nqb, nkb)) < 0.45
+        mask[1] = False                              # an empty query block
+        mask[0, nkb - 1] = True                      # the ragged key tail is reached
+        mask[nqb - 1, 0] = True
+    assert (mask != mask.T).any() if nqb == nkb else True
+    o, lse = oracle.block_sparse_attention(q, k, v, mask, block, scale=0.7)
+    ob, lb = _brute_block_sparse(q, k, v, mask, block, 0.7)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    assert (np.isneginf(lse) == np.isneginf(lb)).all()
+    fin = ~np.isneginf(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
+    assert np.isneginf(lse[block:2 * block]).all() and (o[block:2 * block] == 0).all()
