@@ -225,7 +225,8 @@ int32_t sva_block_means(const void *x, int32_t dtype, int32_t batch, int32_t hea
  *   kept_count [bh][n_qblocks] int32 in [0, n_kblocks]
  *   kept_idx   [bh][n_qblocks][kept_stride] int32; the first kept_count
  *              entries are distinct K block ids in [0, n_kblocks)
- *   scale      logit scale (1/sqrt(d) for standard attention)
+ *   scale      logit scale, finite and >= 0 (1/sqrt(d) for standard
+ *              attention); a negative scale is rejected with SVA_EINVAL
  *   o          [bh][n_q][d] OUT, o_dtype SVA_BF16 or SVA_F32
  *   lse        [bh][n_q] fp32 OUT, natural log; may be NULL
  * ------------------------------------------------------------------------ */

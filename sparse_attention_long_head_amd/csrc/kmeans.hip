@@ -70,8 +70,13 @@ __device__ __forceinline__ int cswz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
+constexpr int kCandWaves = 4;                   // waves per workgroup of the candidate pass
+constexpr int kCandTok = 32 * kCandWaves;       // sorted positions per workgroup (128)
+constexpr int kNbrMaxC = 4096;                  // largest C of the candidate path
+
 struct KmLayout {
-  size_t chi, clo, nh, ctl, flags, tflags, tcount, pcount, perm, offsets, sort, total;
+  size_t chi, clo, nh, ctl, flags, tflags, qids, tcount, pcount, perm, seg, offsets, rad, nbr,
+      tun, sort, total;
 };
 
 // ctl holds the bh refine-queue lengths
@@ -90,10 +95,18 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   L.ctl = take(static_cast<size_t>(bh) * 4);
   L.flags = take(static_cast<size_t>(bh) * n * 8);
   L.tflags = take(static_cast<size_t>(bh) * n * 8);
-  L.tcount = take(static_cast<size_t>(bh) * ((n + kResTok - 1) / kResTok) * 4);   // either pass
-  L.pcount = take(static_cast<size_t>(bh) * ((n + kTokTile - 1) / kTokTile) * 4);
+  L.qids = take(static_cast<size_t>(bh) * n * 8);     // candidate ids of queued rows
+  L.tcount = take(static_cast<size_t>(bh) * ((n + kResTok - 1) / kResTok) * 4);   // any pass
+  L.pcount = take(static_cast<size_t>(bh) * ((n + kCandTok - 1) / kCandTok) * 4);
   L.perm = take(static_cast<size_t>(bh) * n * 4);
+  L.seg = take(static_cast<size_t>(bh) * n * 4);
   L.offsets = take(static_cast<size_t>(bh) * (c + 1) * 4);
+  L.rad = take(static_cast<size_t>(bh) * cpad * 4);
+  // neighbour rows [bh][cpad][cpad/32] and tile unions [bh][tiles][cpad/32]
+  // (candidate path, C <= kNbrMaxC)
+  const size_t nw = c <= kNbrMaxC ? cpad / 32 : 0;
+  L.nbr = take(static_cast<size_t>(bh) * cpad * nw * 4);
+  L.tun = take(static_cast<size_t>(bh) * ((n + kCandTok - 1) / kCandTok) * nw * 4);
   L.sort = take(sort_ws_bytes(bh, n, c));
   L.total = off;
   return L;
@@ -939,6 +952,546 @@ __global__ __launch_bounds__(kThreads) void km_queue_join_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Candidate path (every iteration after the first, for C <= kNbrMaxC).  The
+// assignment of the previous iteration says which cluster a each token was
+// in; the mean pass of that iteration bounds R_a >= max ||x - c_a|| over those
+// tokens for the new centroid c_a.  For any token x of a and any cluster j with
+// ||c_a - c_j|| > 2 R_a, the triangle inequality gives ||x - c_j|| >=
+// ||c_a - c_j|| - ||x - c_a|| > R_a >= ||x - c_a||, so j is strictly farther
+// than a and can be neither the argmin nor tied with it.  The argmin over all
+// clusters is therefore the argmin over N(a) = {j : ||c_a - c_j|| <= 2 R_a},
+// which holds a itself, and over any superset of N(a).
+//   km_nbr_kernel       the neighbour bit matrix: bit j of row a is set for j
+//                       in N(a) (up to a rigorous error bound, always on the
+//                       side of setting it)
+//   km_tile_union_kernel  for each tile of kCandTok positions of the previous
+//                       iteration's sorted order, the OR of the rows of the
+//                       tile's clusters (a run of ids, since the order is
+//                       sorted by cluster)
+//   km_assign_cand_kernel  the tile's tokens against the clusters of its union
+//   km_settle_kernel    the rows it left undecided, in fp64, over the union
+// ---------------------------------------------------------------------------
+
+// Neighbour bits.  A workgroup takes kNbrWaves tiles of 32 clusters a of a
+// slice (one per wave, held as MFMA B operands, hi and lo split) and streams
+// every tile of 32 clusters j through two LDS buffers (direct global->LDS
+// copies, swizzled as in the main pass).  The Gram block G = hi_j.hi_a +
+// lo_j.hi_a + hi_j.lo_a runs on MFMA (clusters j on the accumulator rows, the
+// lane's cluster a on its column), D = ||c_a||^2 + ||c_j||^2 - 2 G, and bit j
+// is cleared only if D - errD > 4 R_a^2, with errD a rigorous bound of
+// |D - ||c_a - c_j||^2|:
+// * the split leaves c = hi + lo + res with |res| <= 2^-18 |c| per element, so
+//   the three dropped products (lo.lo and the two res terms) are below
+//   3.1 * 2^-18 |c_a||c_j|;
+// * the 3d accumulated products sum, in magnitude, to at most 1.03 |c_a||c_j|
+//   and each addition loses at most one unit (2^-23) of that;
+// * the fp32 norms (rounded from fp64), their sum and the final subtraction
+//   lose at most 4 * 2^-24 (|c_a|^2 + |c_j|^2);
+// all with a 1.25 margin.
+constexpr int kNbrWaves = 4;
+constexpr int kNbrJt = 4;                       // tiles of clusters j per workgroup
+template <int D>
+__global__ __launch_bounds__(64 * kNbrWaves) void km_nbr_kernel(
+    const uint16_t *__restrict__ chi, const uint16_t *__restrict__ clo,
+    const float *__restrict__ nh, const float *__restrict__ rad, int c, int cpad,
+    uint32_t *__restrict__ nbr) {
+  constexpr int NS = D / 16;
+  constexpr int PPR = D / 8;                        // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;                     // rows per 1 KB wave copy
+  constexpr int BPS = 32 / RPI;                     // wave copies per split per tile
+  constexpr int CPW = 2 * BPS / kNbrWaves;          // wave copies per wave per tile
+  static_assert(CPW >= 1 && CPW < 8, "copy split");
+  constexpr int kSplitB = 32 * D * 2;
+  constexpr int kBufB = 2 * kSplitB;
+  __shared__ __attribute__((aligned(16))) uint16_t sJ[2][2][32 * D];   // [buffer][split]
+  __shared__ __attribute__((aligned(16))) float sNj[2][64];            // [32, 64): padding
+  const int bh = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int nw = cpad / 32;
+  const int jt0 = blockIdx.y * kNbrJt, jt1 = min(nw, jt0 + kNbrJt);
+  const size_t cb = static_cast<size_t>(bh) * cpad;
+  const int a0 = (blockIdx.x * kNbrWaves + wave) * 32;
+  const bool wave_ok = a0 < cpad;                  // wave-uniform
+  const int a = wave_ok ? a0 + col : col;
+  bf16x8 bh_[NS], bl_[NS];
+  {
+    const uint16_t *pa = chi + (cb + a) * D + h * 8, *pb = clo + (cb + a) * D + h * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bh_[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(pa + s * 16));
+      bl_[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(pb + s * 16));
+    }
+  }
+  const float na = -2.f * nh[cb + a];
+  const float r = rad[cb + a];
+  const float lim = 4.f * r * r * (1.f + 0x1p-20f);
+  const int cp_rsub = lane / PPR, cp_piece = lane % PPR;
+  auto issue = [&](int jt, int b) {
+    {
+      const float *src = nh + cb + jt * 32 + (lane & 31);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)&sNj[b][0], 4, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int blk = wave * CPW + j;
+      const int sp = blk / BPS, rb = blk % BPS;
+      const int rr = rb * RPI + cp_rsub;
+      const size_t goff = (cb + jt * 32 + rr) * D + ((cp_piece ^ cswz<D>(rr)) << 3);
+      const uint16_t *src = (sp ? clo : chi) + goff;
+      uint16_t *dst = &sJ[b][sp][rb * RPI * D];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+  };
+  uint32_t ka[NS];
+  const uint32_t sj0 = lds_offset(&sJ[0][0][0]);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ka[s] = sj0 + col * D * 2 + (((2 * s + h) ^ cswz<D>(col)) << 4);
+  const uint32_t nja = lds_offset(&sNj[0][0]) + 16 * h;
+  constexpr float kG = 2.f * (3.1f * 0x1p-18f + 3.f * D * 0x1p-23f * 1.03f);
+  auto compute = [&](auto bufc, int jt) {
+    constexpr int B = decltype(bufc)::value;
+    f32x4 n4[4];
+    lds_read_f32x4x4<B * 256, 32>(n4, nja);
+    f32x16 g;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) g[i] = 0.f;
+    bf16x8 ah[NS], al[NS];
+    lds_read_frags<B * kBufB>(ah, ka);
+    lds_read_frags<B * kBufB + kSplitB>(al, ka);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) g = mfma32x32x16(ah[s], bh_[s], g);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) g = mfma32x32x16(al[s], bh_[s], g);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) g = mfma32x32x16(ah[s], bl_[s], g);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = acc_row(i, h);
+      const float nj = -2.f * n4[i >> 2][i & 3];
+      const float dd = (na + nj) - 2.f * g[i];
+      const float err = 1.25f * (kG * sqrtf(na * nj) + 0x1p-22f * (na + nj));
+      const int j = jt * 32 + row;
+      const bool need = j < c && (j == a || dd - err <= lim);
+      bits |= need ? (1u << row) : 0u;
+    }
+    bits |= __shfl_xor(bits, 32);                      // both halves: all 32 rows
+    if (wave_ok && h == 0 && a < c) nbr[(cb + a) * nw + jt] = bits;
+  };
+  issue(jt0, 0);
+  if (jt0 + 1 < jt1) issue(jt0 + 1, 1);
+  for (int jt = jt0; jt < jt1; ++jt) {
+    const int b = (jt - jt0) & 1;
+    if (jt + 1 < jt1) wait_vmcnt<CPW + 1>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (b) compute(std::integral_constant<int, 1>{}, jt);
+    else compute(std::integral_constant<int, 0>{}, jt);
+    if (jt + 2 < jt1) {
+      lds_barrier();                                   // every wave is done with buffer b
+      issue(jt + 2, b);
+    }
+  }
+}
+
+// Tile unions: word w of tile t = OR of word w of the rows of the tile's
+// clusters a0 .. a1 (the clusters of its first and last sorted positions).
+__global__ __launch_bounds__(64) void km_tile_union_kernel(
+    const int32_t *__restrict__ seg, const uint32_t *__restrict__ nbr, int n, int c, int cpad,
+    int tph, uint32_t *__restrict__ tun) {
+  const int tile = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  const int nw = cpad / 32;
+  const int base = tile * kCandTok, last = min(n, base + kCandTok) - 1;
+  const int32_t *sg = seg + static_cast<size_t>(bh) * n;
+  const int a0 = min(max(sg[base], 0), c - 1), a1 = min(max(sg[last], 0), c - 1);
+  const uint32_t *rows = nbr + static_cast<size_t>(bh) * cpad * nw;
+  for (int w = lane; w < nw; w += 64) {
+    uint32_t m = 0;
+    for (int a = a0; a <= a1; ++a) m |= rows[static_cast<size_t>(a) * nw + w];
+    tun[(static_cast<size_t>(bh) * tph + tile) * nw + w] = m;
+  }
+}
+
+// The union of a tile as ascending ids in LDS, from word `m` of its bit mask
+// held by thread m's index (threads nw and above hold 0); returns its size
+// (ids past cap are not stored).  All kThr threads must call it.
+template <int kThr>
+__device__ int tile_union_ids(uint32_t m, int32_t *ids, int cap, int32_t *wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cnt = __popc(m);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  lds_barrier();
+  int pre = 0, nu = 0;
+#pragma unroll
+  for (int w = 0; w < kThr / 64; ++w) {
+    pre += w < wave ? wsum[w] : 0;
+    nu += wsum[w];
+  }
+  int k = pre + incl - cnt;
+  for (uint32_t b = m; b; b &= b - 1, ++k)
+    if (k < cap) ids[k] = 32 * tid + __builtin_ctz(b);
+  lds_barrier();
+  return nu;
+}
+
+// Assign pass over candidates.  A workgroup takes kCandTok consecutive
+// positions of the previous iteration's sorted order, one group of 32 tokens
+// per wave held as MFMA B operands.  The tile's union (ascending ids; every
+// cluster when it is too large) is gathered 32 clusters at a time ("virtual
+// tiles": hi and lo split, swizzled as in the main pass) into two LDS buffers
+// by direct global->LDS copies, the next tile's copies in flight while a tile
+// is computed.  Every value's tracking, error bound and decision (decided /
+// two candidates / queued) are those of km_assign_main_kernel, the tile of a
+// value being its virtual tile.  Queued and pair rows go to the workgroup's
+// region of tflags as in the main pass.
+constexpr int kUnionCap = 1024;                 // union ids held in LDS (more: every cluster)
+template <int D>
+__global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
+    const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
+    const uint16_t *__restrict__ clo, const float *__restrict__ nh,
+    const int32_t *__restrict__ perm, const uint32_t *__restrict__ tun,
+    int32_t *__restrict__ assign, int2 *__restrict__ tflags, uint64_t *__restrict__ qids,
+    int32_t *__restrict__ tcount, int32_t *__restrict__ pcount, int nbh, int tph) {
+  constexpr int NS = D / 16;
+  constexpr int kThr = 64 * kCandWaves;
+  constexpr int PPR = D / 8;                        // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;                     // rows per 1 KB wave copy
+  constexpr int BPS = 32 / RPI;                     // wave copies per split per tile
+  constexpr int CPW = 2 * BPS / kCandWaves;         // wave copies per wave per tile
+  static_assert(CPW >= 1 && CPW < 8, "copy split");
+  constexpr int kSplitB = 32 * D * 2;
+  constexpr int kBufB = 2 * kSplitB;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][2][32 * D];   // [buffer][split]
+  __shared__ __attribute__((aligned(16))) float sN[2][64];   // [32, 64): copy padding
+  __shared__ int32_t sU[kUnionCap];
+  __shared__ int32_t s_wsum[kCandWaves];
+  __shared__ int32_t s_wq[kCandWaves], s_wp[kCandWaves];
+  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (k8 / tph);
+  const int tile = k8 % tph;
+  if (bh >= nbh) return;   // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const size_t cb = static_cast<size_t>(bh) * cpad;
+  const int nw = cpad / 32;
+  const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
+  int32_t *as = assign + static_cast<size_t>(bh) * n;
+  const int base = tile * kCandTok;
+  const int last = base + min(kCandTok, n - base) - 1;
+
+  // the tile's union mask (loaded first: loads complete in order, and this one
+  // is waited for before the token rows are needed); this wave's 32 tokens as
+  // B operands, in flight while the union is compacted (the barriers below
+  // wait for LDS only)
+  const uint32_t m_own = tid < nw ? tun[(static_cast<size_t>(bh) * tph + tile) * nw + tid] : 0u;
+  // max ||c|| of the slice (with margin), as in the main pass: eight
+  // independent loads per lane at a time
+  float mn = 0.f;
+  for (int j0 = 0; j0 < c; j0 += 8 * 64) {
+    float v8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * 64 + lane;
+      v8[u] = j < c ? nh[cb + j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mn = fminf(mn, v8[u]);
+  }
+  const int p = base + wave * 32 + col;
+  const bool tv = p < n;
+  const int tok = perm[static_cast<size_t>(bh) * n + (tv ? p : last)];
+  bf16x8 xf[NS];
+  {
+    const uint16_t *row = xb + static_cast<size_t>(tok) * D + h * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      xf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + s * 16));
+  }
+  int nu = tile_union_ids<kThr>(m_own, sU, kUnionCap, s_wsum);
+  const bool ids_all = nu > kUnionCap || nu >= c;
+  if (ids_all) nu = c;
+  const int nv = (nu + 31) / 32;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mn = fminf(mn, __shfl_xor(mn, o));
+  const float cm = sqrtf(-2.f * mn) * (1.f + 0x1p-20f);
+
+  // virtual tile v into buffer b: wave copy j of the tile fills LDS bytes
+  // [1 KB * blk, +1 KB) of split blk / BPS; lane l fills physical piece l % PPR of
+  // row RPI * (blk % BPS) + l / PPR (the row's logical piece (l % PPR) ^ swizzle);
+  // each wave also copies the tile's 32 -||c||^2/2 values, so every wave has
+  // CPW + 1 copies per tile in flight (padding rows are masked in compute)
+  const int cp_rsub = lane / PPR, cp_piece = lane % PPR;
+  auto uid = [&](int slot) { return ids_all ? min(slot, c - 1) : sU[min(slot, nu - 1)]; };
+  auto issue = [&](int v, int b) {
+    {
+      const float *src = nh + cb + uid(v * 32 + (lane & 31));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)&sN[b][0], 4, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int blk = wave * CPW + j;
+      const int sp = blk / BPS, rb = blk % BPS;
+      const int r = rb * RPI + cp_rsub;
+      const int id = uid(v * 32 + r);
+      const size_t goff = (cb + id) * D + ((cp_piece ^ cswz<D>(r)) << 3);
+      const uint16_t *src = (sp ? clo : chi) + goff;
+      uint16_t *dst = &sA[b][sp][rb * RPI * D];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+  };
+  uint32_t ka[NS];
+  const uint32_t sa0 = lds_offset(&sA[0][0][0]);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ka[s] = sa0 + col * D * 2 + (((2 * s + h) ^ cswz<D>(col)) << 4);
+  const uint32_t na = lds_offset(&sN[0][0]) + 16 * h;
+
+  // the error bound of this token's values (x row norm, slice max ||c||)
+  float px = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const u32x4 u = __builtin_bit_cast(u32x4, xf[s]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x2 w2 = __builtin_bit_cast(bf16x2, u[j]);
+      px = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, px, false);
+    }
+  }
+  px += __shfl_xor(px, 32);
+  const float nx = sqrtf(px) * (1.f + 0x1p-10f) + 0x1p-60f;
+  const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx * cm +
+                  (2.f * D) * 0x1p-23f * (0.5f * cm * cm + 1.02f * nx * cm) +
+                  0x1p-19f * (nx * cm + 0.5f * cm * cm);
+  const float two_e = 2.f * 1.25f * e;
+
+  // candidates of the first two virtual tiles: slots whose value reaches this
+  // lane half's best so far minus 2E (a superset of those that reach the
+  // final best minus 2E, which hold the argmin)
+  float b1 = -INFINITY, b2 = -INFINITY, b3 = -INFINITY;
+  int t1 = 0, t2 = 0;
+  uint32_t cmask[2] = {0u, 0u};
+  auto compute = [&](auto bufc, int v) {
+    constexpr int B = decltype(bufc)::value;
+    f32x4 n4[4];
+    lds_read_f32x4x4<B * 256, 32>(n4, na);
+    f32x16 acc;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        acc[i] = v * 32 + acc_row(i, h) < nu ? n4[g][j] : -FLT_MAX;   // padding rows
+      }
+    bf16x8 af[NS];
+    lds_read_frags<B * kBufB>(af, ka);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = mfma32x32x16(af[s], xf[s], acc);
+    lds_read_frags<B * kBufB + kSplitB>(af, ka);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = mfma32x32x16(af[s], xf[s], acc);
+    const float p1 = b1, p2 = b2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float we = __int_as_float((__float_as_int(acc[i]) & ~15) | i);
+      b3 = __builtin_amdgcn_fmed3f(b2, b3, we);
+      b2 = __builtin_amdgcn_fmed3f(b1, b2, we);
+      b1 = __builtin_elementwise_maximum(b1, we);
+    }
+    const bool new1 = b1 != p1;
+    t2 = b2 == p2 ? t2 : ((new1 && b2 == p1) ? t1 : v);
+    t1 = new1 ? v : t1;
+    if (v < 2) {
+      const float thr = b1 - two_e;
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m |= acc[i] >= thr ? (1u << acc_row(i, h)) : 0u;
+      cmask[v] = m;
+    }
+  };
+
+  issue(0, 0);
+  if (nv > 1) issue(1, 1);
+  for (int v = 0; v < nv; ++v) {
+    // tile v has landed once only tile v+1's copies are outstanding (the token
+    // rows, issued earlier, have landed too)
+    if (v + 1 < nv) wait_vmcnt<CPW + 1>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (v & 1) compute(std::integral_constant<int, 1>{}, v);
+    else compute(std::integral_constant<int, 0>{}, v);
+    if (v + 2 < nv) {
+      lds_barrier();                                   // every wave is done with buffer v & 1
+      issue(v + 2, v & 1);
+    }
+  }
+
+  const int i1 = uid(t1 * 32 + acc_row(__float_as_int(b1) & 15, h));
+  const int i2 = uid(t2 * 32 + acc_row(__float_as_int(b2) & 15, h));
+  const float ob1 = __shfl_xor(b1, 32), ob2 = __shfl_xor(b2, 32), ob3 = __shfl_xor(b3, 32);
+  const int oi1 = __shfl_xor(i1, 32), oi2 = __shfl_xor(i2, 32);
+  const bool other = ob1 > b1 || (ob1 == b1 && oi1 < i1);
+  const float nb1 = fmaxf(b1, ob1);
+  const int ival = other ? oi1 : i1;
+  const float lo1 = fminf(b1, ob1), hi2 = fmaxf(b2, ob2);
+  const float nb2 = fmaxf(lo1, hi2);
+  const int ival2 = lo1 >= hi2 ? (other ? i1 : oi1) : (b2 >= ob2 ? i2 : oi2);
+  const float nb3 = fmaxf(fmaxf(fminf(b1, ob2), fminf(b2, ob1)), fmaxf(b3, ob3));
+  const bool decided = nb1 - nb2 > two_e;
+  const bool two = !decided && nb1 - nb3 > two_e;
+  if (h == 0 && tv && decided) as[tok] = ival;
+  const bool queued = h == 0 && tv && !decided && !two;
+  const bool paired = h == 0 && tv && two;
+  // a queued row with at most four candidates (both halves, at most two
+  // virtual tiles) lists their ids; otherwise the settle pass takes the union
+  const uint32_t m0 = cmask[0] | __shfl_xor(cmask[0], 32);
+  const uint32_t m1 = cmask[1] | __shfl_xor(cmask[1], 32);
+  const int ncand = nv <= 2 ? __popc(m0) + __popc(m1) : 99;
+  uint64_t listed = 0;
+  int nlisted = 0;
+  if (queued && ncand <= 4) {
+    for (int vv = 0; vv < 2; ++vv)
+      for (uint32_t m = vv ? m1 : m0; m; m &= m - 1, ++nlisted)
+        listed |= static_cast<uint64_t>(uid(vv * 32 + __builtin_ctz(m))) << (16 * nlisted);
+  }
+  const uint64_t qm = __ballot(queued), pmk = __ballot(paired);
+  const uint64_t wm = __ballot(queued && nlisted == 0);
+  if (lane == 0) {
+    s_wq[wave] = __popcll(qm) | (__popcll(wm) << 16);
+    s_wp[wave] = __popcll(pmk);
+  }
+  __syncthreads();
+  // s_wq: queued rows of the wave (bits 0-15) and those without listed ids
+  // (bits 16-31); the tile's count keeps the same layout
+  int q = base, pp = 0, tot = 0, ptot = 0, wide = 0;
+#pragma unroll
+  for (int w = 0; w < kCandWaves; ++w) {
+    q += w < wave ? (s_wq[w] & 0xffff) : 0;
+    pp += w < wave ? s_wp[w] : 0;
+    tot += s_wq[w] & 0xffff;
+    wide += s_wq[w] >> 16;
+    ptot += s_wp[w];
+  }
+  const uint64_t lt = (1ull << lane) - 1;
+  if (queued) {
+    const size_t at = static_cast<size_t>(bh) * n + q + __popcll(qm & lt);
+    tflags[at] = int2{tok, nlisted};
+    qids[at] = listed;
+  }
+  if (paired)
+    tflags[static_cast<size_t>(bh) * n + last - (pp + __popcll(pmk & lt))] =
+        int2{tok, (ival << 16) | ival2};
+  if (tid == 0) {
+    tcount[static_cast<size_t>(bh) * tph + tile] = tot | (wide << 16);
+    pcount[static_cast<size_t>(bh) * tph + tile] = ptot;
+  }
+}
+
+// Settle the rows the candidate pass left undecided, exactly, in fp64: a pair
+// row compares its two clusters, a queued row the (up to four) clusters the
+// assign pass listed for it, or, when it listed none, every cluster of the
+// tile's union (a superset of the row's own candidates).  One workgroup per
+// token tile; a group of 8 lanes per row (D/8 dimensions per lane, each lane's
+// terms added in ascending order, the lanes in a fixed butterfly), four
+// candidates loaded at a time; the smallest distance wins, ties to the lowest
+// id.
+template <int D>
+__global__ __launch_bounds__(kThreads) void km_settle_kernel(
+    const uint16_t *__restrict__ x, int n, int c, int cpad, const float *__restrict__ cent,
+    const uint32_t *__restrict__ tun, const int2 *__restrict__ tflags,
+    const uint64_t *__restrict__ qids, const int32_t *__restrict__ tcount,
+    const int32_t *__restrict__ pcount, int32_t *__restrict__ assign,
+    int32_t *__restrict__ n_refined, int nbh, int tph) {
+  constexpr int LPR = 8;                     // lanes per row
+  constexpr int DPL = D / LPR;               // dimensions per lane (8 or 16)
+  constexpr int XQ = DPL / 8;                // 16-byte pieces of x per lane
+  constexpr int CQ = 2 * XQ;                 // 16-byte pieces of a centroid per lane
+  constexpr int GPB = kThreads / LPR;        // rows in flight per workgroup
+  constexpr int U = 4;                       // candidates loaded at a time
+  __shared__ int32_t sU[kUnionCap];
+  __shared__ int32_t s_wsum[kThreads / 64];
+  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (k8 / tph);
+  const int tile = k8 % tph;
+  if (bh >= nbh) return;
+  const int tq = tcount[static_cast<size_t>(bh) * tph + tile];
+  const int nq = tq & 0xffff, nwide = tq >> 16;
+  const int np = pcount[static_cast<size_t>(bh) * tph + tile];
+  if (nq + np == 0) return;                  // uniform
+  const int tid = threadIdx.x, sub = tid % LPR, grp = tid / LPR;
+  const int base = tile * kCandTok;
+  const int last = base + min(kCandTok, n - base) - 1;
+  const int nw = cpad / 32;
+  const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
+  const float *cs = cent + static_cast<size_t>(bh) * c * D;
+  int32_t *as = assign + static_cast<size_t>(bh) * n;
+  int nu = c;
+  bool all = true;
+  if (nwide > 0) {                           // uniform
+    const uint32_t m_own =
+        tid < nw ? tun[(static_cast<size_t>(bh) * tph + tile) * nw + tid] : 0u;
+    nu = tile_union_ids<kThreads>(m_own, sU, kUnionCap, s_wsum);
+    all = nu > kUnionCap || nu >= c;
+    if (all) nu = c;
+  }
+  for (int k = grp; k < nq + np; k += GPB) {   // uniform over the row's lanes
+    const bool pair = k >= nq;
+    const size_t at = static_cast<size_t>(bh) * n + (pair ? last - (k - nq) : base + k);
+    const int2 e = tflags[at];
+    const uint64_t li = pair ? 0ull : qids[at];
+    u32x4 xv[XQ];
+#pragma unroll
+    for (int i = 0; i < XQ; ++i)
+      xv[i] = reinterpret_cast<const u32x4 *>(xb + static_cast<size_t>(e.x) * D)[sub * XQ + i];
+    // candidate j of this row: the pair's two, the listed ids, or the union
+    const int cnt = pair ? 2 : (e.y > 0 ? e.y : nu);
+    auto cand_id = [&](int j) {
+      if (j >= cnt) return -1;
+      if (pair) return j == 0 ? (e.y >> 16) & 0xffff : e.y & 0xffff;
+      if (e.y > 0) return static_cast<int>((li >> (16 * j)) & 0xffff);
+      return all ? j : sU[j];
+    };
+    double bd = INFINITY;
+    int bi = 0x7fffffff;
+    for (int j0 = 0; j0 < cnt; j0 += U) {
+      int id[U];
+      f32x4 cv[U][CQ];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        id[u] = cand_id(j0 + u);
+        const f32x4 *cr = reinterpret_cast<const f32x4 *>(cs + static_cast<size_t>(id[u] >= 0 ? id[u] : 0) * D);
+#pragma unroll
+        for (int i = 0; i < CQ; ++i) cv[u][i] = cr[sub * CQ + i];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        double s2 = 0.0;
+#pragma unroll
+        for (int t = 0; t < DPL; ++t) {
+          const float xf32 = bf16_bits_to_f32(static_cast<uint16_t>(xv[t >> 3][(t >> 1) & 3] >> (16 * (t & 1))));
+          const float cf32 = cv[u][t >> 2][t & 3];
+          const double df = static_cast<double>(xf32) - static_cast<double>(cf32);
+          s2 = fma(df, df, s2);
+        }
+#pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) s2 += __shfl_xor(s2, o);
+        if (id[u] >= 0 && (s2 < bd || (s2 == bd && id[u] < bi))) {
+          bd = s2;
+          bi = id[u];
+        }
+      }
+    }
+    if (sub == 0) as[e.x] = bi;
+  }
+  if (n_refined != nullptr && tid == 0) atomicAdd(n_refined, nq + np);
+}
+
+// ---------------------------------------------------------------------------
 // fp64 assignment (fp32 inputs): exact distances to every cluster
 // ---------------------------------------------------------------------------
 template <int D>
@@ -995,7 +1548,8 @@ template <int D, bool BF16, int WPC>
 __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
     const void *__restrict__ x, int n, int c, int cpad, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, float *__restrict__ cent, uint16_t *__restrict__ chi,
-    uint16_t *__restrict__ clo, float *__restrict__ nh, int mode, int ncl) {
+    uint16_t *__restrict__ clo, float *__restrict__ nh, float *__restrict__ rad, int mode,
+    int ncl) {
   constexpr int EB = BF16 ? 2 : 4;           // element bytes
   constexpr int EPT = 16 / EB;               // elements per 16-byte piece
   constexpr int TPR = D / EPT;               // lanes per row
@@ -1004,6 +1558,7 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
   static_assert(TPR <= 64 && 64 % TPR == 0 && (64 / RG) % U == 0, "row layout");
   static_assert(WPC == 1 || WPC == kMeanWaves, "waves per cluster");
   __shared__ double s_part[WPC > 1 ? WPC : 1][WPC > 1 ? D : 1];
+  __shared__ float s_rmax[WPC > 1 ? WPC : 1][WPC > 1 ? TPR : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wc = WPC > 1 ? wave : 0;         // this wave's rank within its cluster
   // slices in reverse launch order: the assign pass just before walked them in
@@ -1017,10 +1572,20 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
   const size_t crow = (static_cast<size_t>(bh) * c + cl) * D + pc * EPT;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) val[e] = real ? cent[crow + e] : 0.f;
+  // radius bound (bf16 inputs, mean + prep mode): R >= max ||x - c_new|| over
+  // the cluster's rows, from the old centroid: ||x - c_new|| <= ||x - c_old|| +
+  // ||c_old - c_new||.  Each lane keeps the largest sum over its EPT
+  // coordinates of (x - c_old)^2 among its rows; the lanes' maxima added over
+  // the TPR pieces of a row bound the largest row sum from above.
+  const bool want_r = BF16 && rad != nullptr && mode == 1;
+  float rmax = 0.f;
   if (mode != 0 && real) {
     const int st = offsets[static_cast<size_t>(bh) * (c + 1) + cl];
     const int en = offsets[static_cast<size_t>(bh) * (c + 1) + cl + 1];
     if (en > st) {                           // uniform over the cluster's waves
+      float cold[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) cold[e] = val[e];
       double acc[EPT];
 #pragma unroll
       for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
@@ -1048,13 +1613,17 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             if (pr[u] < 0) continue;
+            float dd = 0.f;
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
               float f;
               if constexpr (BF16) f = bf16_bits_to_f32(static_cast<uint16_t>(buf[u][e >> 1] >> (16 * (e & 1))));
               else f = __uint_as_float(buf[u][e]);
               acc[e] += static_cast<double>(f);
+              const float t = f - cold[e];
+              dd = fmaf(t, t, dd);
             }
+            rmax = want_r ? fmaxf(rmax, dd) : rmax;
           }
         }
       }
@@ -1083,8 +1652,37 @@ __global__ __launch_bounds__(64 * kMeanWaves) void km_mean_kernel(
 #pragma unroll
         for (int e = 0; e < EPT; ++e) cent[crow + e] = val[e];
       }
+      if (want_r) {
+        // the piece's largest partial over the row groups, then the waves
+#pragma unroll
+        for (int off = TPR; off < 64; off <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+        if constexpr (WPC > 1) {
+          if (g == 0) s_rmax[wc][pc] = rmax;
+          __syncthreads();
+#pragma unroll
+          for (int w = 0; w < WPC; ++w) rmax = fmaxf(rmax, s_rmax[w][pc]);
+        }
+        // sum over the pieces: R_old^2; and ||c_old - c_new||^2 likewise
+        float dc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          const float t = cold[e] - val[e];
+          dc = fmaf(t, t, dc);
+        }
+#pragma unroll
+        for (int off = 1; off < TPR; off <<= 1) {
+          rmax += __shfl_xor(rmax, off);
+          dc += __shfl_xor(dc, off);
+        }
+        // fp32 roundings of the sums (under 2^-20 relative here) are covered
+        // by the 2^-12 margins
+        rmax = sqrtf(rmax * (1.f + 0x1p-12f)) + sqrtf(dc * (1.f + 0x1p-12f));
+        rmax *= 1.f + 0x1p-12f;
+      }
     }
   }
+  if (want_r && lane == 0 && wc == 0 && cl < cpad)
+    rad[static_cast<size_t>(bh) * cpad + cl] = rmax;
   if (mode == 2 || wc != 0) return;
   // prep for the next assignment (first wave of the cluster): hi/lo split,
   // -||c||^2/2
@@ -1124,15 +1722,25 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   int32_t *ctl = reinterpret_cast<int32_t *>(w + L.ctl);   // [bh] refine-queue lengths
   int2 *flags = reinterpret_cast<int2 *>(w + L.flags);
   int2 *tflags = reinterpret_cast<int2 *>(w + L.tflags);
+  uint64_t *qids = reinterpret_cast<uint64_t *>(w + L.qids);
   int32_t *tcount = reinterpret_cast<int32_t *>(w + L.tcount);
   int32_t *pcount = reinterpret_cast<int32_t *>(w + L.pcount);
   int32_t *perm = reinterpret_cast<int32_t *>(w + L.perm);
+  int32_t *seg = reinterpret_cast<int32_t *>(w + L.seg);
   int32_t *offsets = reinterpret_cast<int32_t *>(w + L.offsets);
+  float *rad = reinterpret_cast<float *>(w + L.rad);
+  uint32_t *nbr = reinterpret_cast<uint32_t *>(w + L.nbr);
+  uint32_t *tun = reinterpret_cast<uint32_t *>(w + L.tun);
+  // the candidate path for tables too large for the resident pass
+  const bool cand_ok = a.c <= kNbrMaxC && (a.c + 31) / 32 > kResTiles;
   void *sort_ws = w + L.sort;
   const int cpad = (a.c + 31) / 32 * 32;
   const bool bf16 = a.dtype == SVA_BF16;
   const int tph = (a.n + kTokTile - 1) / kTokTile;
   const dim3 tok_grid(8 * tph * ((a.bh + 7) / 8));
+  // candidate path: 256 sorted positions per workgroup, slices dealt to XCDs
+  const int ctph = (a.n + kCandTok - 1) / kCandTok;
+  const dim3 cand_grid(8 * ctph * ((a.bh + 7) / 8));
   hipError_t e;
 #define SVA_CHECK(x)               \
   do {                             \
@@ -1160,7 +1768,7 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     const dim3 block(64 * kMeanWaves);
 #define SVA_MEAN(B, W)                                                                       \
   hipLaunchKernelGGL((km_mean_kernel<D, B, W>), grid, block, 0, s, a.x, a.n, a.c, cpad, perm, \
-                     offsets, a.centroids, chi, clo, nh, mode, ncl)
+                     offsets, a.centroids, chi, clo, nh, cand_ok ? rad : nullptr, mode, ncl)
     if (bf16) {
       if (wide) SVA_MEAN(true, kMeanWaves);
       else SVA_MEAN(true, 1);
@@ -1178,7 +1786,22 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   }
   for (int it = 0; it < a.iters; ++it) {
     const bool last = it + 1 == a.iters;
-    if (bf16) {
+    if (bf16 && it > 0 && cand_ok) {
+      // the tiles' unions of candidates (neighbour rows built after the
+      // previous iteration's mean pass), the assignment over them, then the
+      // undecided rows in fp64
+      hipLaunchKernelGGL(km_tile_union_kernel, dim3(ctph, a.bh), dim3(64), 0, s, seg, nbr, a.n,
+                         a.c, cpad, ctph, tun);
+      SVA_CHECK(hipGetLastError());
+      hipLaunchKernelGGL((km_assign_cand_kernel<D>), cand_grid, dim3(64 * kCandWaves), 0, s,
+                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, perm,
+                         tun, a.assign, tflags, qids, tcount, pcount, a.bh, ctph);
+      SVA_CHECK(hipGetLastError());
+      hipLaunchKernelGGL((km_settle_kernel<D>), cand_grid, dim3(kThreads), 0, s,
+                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, a.centroids, tun,
+                         tflags, qids, tcount, pcount, a.assign, a.n_refined, a.bh, ctph);
+      SVA_CHECK(hipGetLastError());
+    } else if (bf16) {
       // the pair path (third best tracked) pays once the refine's re-scan is
       // long: with 16 or more centroid tiles (measured break-even between 13 and 16)
       const bool pairs = cpad >= 16 * 32;
@@ -1220,8 +1843,16 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
     }
     // the sort's scan clears the per-slice queue lengths for the next iteration
     SVA_CHECK(launch_cluster_sort(a.assign, a.bh, a.n, a.c, perm, offsets,
-                                  last ? a.sizes : nullptr, sort_ws, s, bf16 ? ctl : nullptr));
+                                  last ? a.sizes : nullptr, sort_ws, s, bf16 ? ctl : nullptr,
+                                  (bf16 && !last && cand_ok) ? seg : nullptr));
     SVA_CHECK(mean((bf16 && !last) ? 1 : 2));
+    if (bf16 && !last && cand_ok) {
+      hipLaunchKernelGGL((km_nbr_kernel<D>),
+                         dim3((cpad / 32 + kNbrWaves - 1) / kNbrWaves,
+                              (cpad / 32 + kNbrJt - 1) / kNbrJt, a.bh),
+                         dim3(64 * kNbrWaves), 0, s, chi, clo, nh, rad, a.c, cpad, nbr);
+      SVA_CHECK(hipGetLastError());
+    }
   }
 #undef SVA_CHECK
 #undef SVA_RES

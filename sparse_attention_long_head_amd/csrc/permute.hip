@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_totals_kernel(
 __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
     const int32_t *__restrict__ assign, const int32_t *__restrict__ rank,
     const int32_t *__restrict__ base, const int32_t *__restrict__ offsets, int n, int c,
-    int tiles, int32_t *__restrict__ perm) {
+    int tiles, int32_t *__restrict__ perm, int32_t *__restrict__ seg) {
   const int bh = blockIdx.y;
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
   const int pos = offsets[static_cast<size_t>(bh) * (c + 1) + key] +
                   base[(static_cast<size_t>(bh) * c + key) * tiles + i / kTile] + rank[row];
   perm[static_cast<size_t>(bh) * n + pos] = i;
+  if (seg != nullptr) seg[static_cast<size_t>(bh) * n + pos] = key;
 }
 
 // dst row r <- src row perm[r] (gather), or dst row perm[r] <- src row r
@@ -189,7 +190,7 @@ size_t sort_ws_bytes(int32_t bh, int32_t n, int32_t c) {
 
 hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int32_t c,
                                int32_t *perm, int32_t *offsets, int32_t *sizes, void *ws,
-                               hipStream_t s, int32_t *clear) {
+                               hipStream_t s, int32_t *clear, int32_t *seg) {
   const int tiles = (n + kTile - 1) / kTile;
   const size_t hist_bytes = align_up(static_cast<size_t>(bh) * c * tiles * 4, 256);
   int32_t *hist = static_cast<int32_t *>(ws);
@@ -208,7 +209,7 @@ hipError_t launch_cluster_sort(const int32_t *assign, int32_t bh, int32_t n, int
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3((n + kThreads - 1) / kThreads, bh),
-                     dim3(kThreads), 0, s, assign, rank, base, offsets, n, c, tiles, perm);
+                     dim3(kThreads), 0, s, assign, rank, base, offsets, n, c, tiles, perm, seg);
   return hipGetLastError();
 }
 

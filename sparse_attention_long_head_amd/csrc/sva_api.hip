@@ -233,7 +233,10 @@ static int32_t check_attn(const char *fn, const void *q, const void *k, const vo
   SVA_TRY(check_slices(fn, batch, heads, n_q));
   if (n_k < 1) return fail(SVA_EINVAL, "%s: n_k must be >= 1", fn);
   SVA_TRY(check_d(fn, d));
-  if (!isfinite(scale)) return fail(SVA_EINVAL, "%s: scale must be finite", fn);
+  // the bf16 kernel's running max is taken on the raw scores and scaled
+  // afterwards, which is the max of the scaled scores only for scale >= 0
+  if (!isfinite(scale) || scale < 0.f)
+    return fail(SVA_EINVAL, "%s: scale must be finite and >= 0 (got %g)", fn, scale);
   return SVA_OK;
 }
 

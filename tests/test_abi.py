@@ -133,6 +133,7 @@ def test_attention_validation(L):
     for i, bad, want in [(0, None, L.SVA_EINVAL), (3, 5, L.SVA_EINVAL), (8, 80, L.SVA_EUNSUPPORTED),
                          (10, 0, L.SVA_EINVAL), (10, 1001, L.SVA_EINVAL), (12, 0, L.SVA_EINVAL),
                          (15, 0, L.SVA_EINVAL), (16, float("nan"), L.SVA_EINVAL),
+                         (16, -0.125, L.SVA_EINVAL), (16, float("-inf"), L.SVA_EINVAL),
                          (18, 9, L.SVA_EINVAL), (21, ws - 1, L.SVA_EWORKSPACE),
                          (13, None, L.SVA_EINVAL)]:
         args = list(ok)
@@ -140,6 +141,9 @@ def test_attention_validation(L):
         assert lib.sva_block_sparse_attn(*args) == want, (i, bad)
     assert lib.sva_full_attn(P, P, P, 1, 1, 2, 10, 10, 64, float("inf"), P, 1, None, None, 0,
                              None) == L.SVA_EINVAL
+    assert lib.sva_full_attn(P, P, P, 1, 1, 2, 10, 10, 64, -1.0, P, 1, None, None, 0,
+                             None) == L.SVA_EINVAL
+    assert ">= 0" in L.last_error()
     assert lib.sva_unpermute(P, None, 1, 1, 1, 10, 64, P, None) == L.SVA_EINVAL
     assert "sva_unpermute" in L.last_error()
 
@@ -150,3 +154,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_valid_call_without_gpu_returns_hip_error(L):
+    """Arguments that pass validation, on a host with no GPU: the launch fails
+    and the call returns SVA_EHIP with HIP's message.  (With a GPU visible the
+    dummy pointers would be dereferenced, so the test only runs without one.)"""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: dummy device pointers must not be launched on")
+    lib = L.lib()
+    assert lib.sva_unpermute(P, P, 1, 1, 2, 10, 64, P, None) == L.SVA_EHIP
+    msg = L.last_error()
+    assert msg.startswith("sva_unpermute") and "device" in msg.lower(), msg
+    ws = lib.sva_full_attn_workspace_bytes(1, 2, 100)
+    assert lib.sva_full_attn(P, P, P, 1, 1, 2, 100, 100, 128, 0.088, P, 1, None, P, ws,
+                             None) == L.SVA_EHIP
+    assert L.last_error().startswith("sva_full_attn")
