@@ -91,8 +91,11 @@ def main() -> int:
     ap.add_argument("--config", default="5s", choices=["5s", "10s", "30s"])
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--workload", default="svg2",
-                    choices=["svg2", "static-ratio", "dynamic-threshold", "kmeans-warm", "sweep"],
-                    help="svg2: k-means clusters + top-p (the default); static-ratio / "
+                    choices=["svg2", "static-mask", "static-ratio", "dynamic-threshold",
+                             "kmeans-warm", "sweep"],
+                    help="svg2: k-means clusters + top-p (the default); static-mask: the fixed "
+                         "radial + random block mask at --static-sparsity, attention alone; "
+                         "static-ratio / "
                          "dynamic-threshold: DynamicRad's two modes on uniform 128-token blocks; "
                          "kmeans-warm: the svg2 layer over a drifting denoising sequence with the "
                          "centroid cache (warm-started k-means)")
@@ -107,6 +110,9 @@ def main() -> int:
                          "dynamic-threshold: threshold on block-mean logits (default 0)")
     ap.add_argument("--ratios", default="1,0.75,0.5",
                     help="static-ratio: kept share of the radial candidates per temporal distance")
+    ap.add_argument("--static-sparsity", type=float, default=0.8,
+                    help="static-mask: share of the 128x128 tiles left out (0.8 = 13,107 of "
+                         "65,536 tiles kept; 0.85 = 9,830)")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -132,6 +138,8 @@ def main() -> int:
         return bench_kmeans_warm(args)
     if args.workload == "sweep":
         return bench_sweep(args)
+    if args.workload == "static-mask":
+        return bench_static_mask(args)
     if args.workload != "svg2":
         return bench_dynamicrad(args)
     cfg = synth.CONFIGS[args.config]
@@ -212,6 +220,8 @@ def main() -> int:
                  "speedup_attention_only": dense_ms / attn_ms,
                  "speedup_whole_layer": dense_ms / ms_step}
 
+    stage_roof = stage_rooflines(layer, t, iq, ik, cfg)
+
     if args.copy_calibration:
         from sparse_attention_long_head_amd import sva_unpermute
         ident = torch.arange(cfg.n, dtype=torch.int32, device=dev).repeat(
@@ -259,9 +269,65 @@ def main() -> int:
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "stage_rooflines": stage_roof,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def stage_rooflines(layer, t, iq, ik, cfg, reps=3):
+    """The layer's other stages timed alone (after the timed steps, same buffers,
+    events on the launch stream), each against the roofline that bounds it:
+    k-means (2 n C d FLOP per iteration on MFMA; its minimum HBM traffic is X read
+    twice per iteration, by the assignment and the mean), the cluster sort (4 B
+    read + 4 B written per row, plus the offsets), the top-p selection (the
+    centroids and sizes read, the mask and kept lists written)."""
+    import torch
+
+    from sparse_attention_long_head_amd import sva_kmeans, sva_permute, sva_select_blocks
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    bh, n, d = cfg.batch * cfg.heads, cfg.n, cfg.d
+    out = {}
+    for name, x, init, c, cent, asg, sz in (("kmeans_q", t["q"], iq, cfg.cq, layer.cent_q,
+                                             layer.assign_q, layer.sizes_q),
+                                            ("kmeans_k", t["k"], ik, cfg.ck, layer.cent_k,
+                                             layer.assign_k, layer.sizes_k)):
+        def run():
+            cent.copy_(init)
+            sva_kmeans(x, c, cfg.iters, cent, asg, sz, ws=layer.ws)
+        ms = timed(run)
+        flops = 2.0 * bh * n * c * d * cfg.iters
+        hbm = 2.0 * cfg.iters * bh * n * d * 2
+        out[name] = {"ms": round(ms, 4), "clusters": c, "iters": cfg.iters,
+                     "algorithmic_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "min_hbm_gbs": round(hbm / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    for name, asg, c, perm, off in (("sort_q", layer.assign_q, cfg.cq, layer.perm_q, layer.off_q),
+                                    ("sort_k", layer.assign_k, cfg.ck, layer.perm_k, layer.off_k)):
+        ms = timed(lambda: sva_permute(asg, c, [], perm, off, ws=layer.ws))
+        nbytes = bh * (8.0 * n + 4.0 * (c + 1))
+        out[name] = {"ms": round(ms, 4), "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5)}
+    ms = timed(lambda: sva_select_blocks(layer.cent_q, layer.sizes_q, layer.cent_k, layer.sizes_k,
+                                         layer.scale, layer.top_p, layer.mask, layer.kept_count,
+                                         layer.kept_idx))
+    nbytes = bh * (4.0 * (cfg.cq + cfg.ck) * (d + 1) + cfg.cq * cfg.ck * (1 + 4) + 4.0 * cfg.cq)
+    out["select"] = {"ms": round(ms, 4), "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                     "bound": "latency (a few kilobytes per slice, sorted per Q cluster)"}
+    return out
 
 
 def _timed(stages, step, steps, warmup):
@@ -314,6 +380,128 @@ def cpu_baseline_dynamicrad(cfg, x, workload, ratios, theta, heads=tuple(range(8
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(heads)} of {cfg.heads} heads: mask, then masked attention of all "
                       f"{cfg.n} query rows in fp64 NumPy; {dt:.1f} s"}
+
+
+def cpu_baseline_static(cfg, x, mask, heads=(0, 1, 2, 3)):
+    """The fp64 oracle's masked attention on a few heads of the same tensors (all
+    query rows); about 10-20 s of host time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
+    sizes = np.diff(synth_offsets(cfg)).astype(np.float64)
+    pairs = float(sizes @ mask.astype(np.float64) @ sizes)
+    t0 = time.perf_counter()
+    for h in heads:
+        q, k, v = (x[n][0, h].astype(np.float64) for n in "qkv")
+        oracle.block_sparse_attention(q, k, v, mask, cfg.block, scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * cfg.d * pairs * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(heads)} of {cfg.heads} heads, masked attention of all {cfg.n} "
+                      f"query rows in fp64 NumPy; {dt:.1f} s"}
+
+
+def synth_offsets(cfg):
+    import synth
+    return synth.uniform_offsets(cfg.n, cfg.block)
+
+
+def bench_static_mask(args) -> int:
+    """The static-mask configuration: i.i.d. N(0,1) Q/K/V at the 5 s clip size
+    and the radial candidate set padded with seeded random tiles to exactly the
+    requested sparsity, one mask for all heads, uniform 128-token blocks in
+    token order.  A step is sva_block_sparse_attn alone (the mask is an input
+    built outside the timed region); dense attention on the same tensors is the
+    reference for the speed-up."""
+    import torch
+
+    import synth
+    from sparse_attention_long_head_amd import sva_block_sparse_attn, sva_full_attn, lib
+
+    cfg = synth.CONFIGS["static"]
+    sp = args.static_sparsity
+    dev = torch.device("cuda:0")
+    log(f"[bench] static-mask: {cfg.n} tokens x {cfg.heads} heads, sparsity {sp}")
+    x = synth.video_qkv(cfg)
+    mask = synth.static_block_mask(cfg, sp)
+    count, idx = synth.mask_to_ell(mask)
+    nb = mask.shape[0]
+    bh = cfg.batch * cfg.heads
+    t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv"}
+    off = torch.from_numpy(synth.uniform_offsets(cfg.n, cfg.block)).to(dev)
+    off = off.expand(cfg.batch, cfg.heads, nb + 1).contiguous()
+    kc = torch.from_numpy(count).to(dev).expand(cfg.batch, cfg.heads, nb).contiguous()
+    ki = torch.from_numpy(idx).to(dev).expand(cfg.batch, cfg.heads, nb, nb).contiguous()
+    scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
+    o = torch.empty_like(t["q"])
+    ws = torch.empty(max(lib().sva_attn_workspace_bytes(cfg.batch, cfg.heads, cfg.n, nb), 1),
+                     dtype=torch.uint8, device=dev)
+    stages = ("attention",)
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        sva_block_sparse_attn(t["q"], t["k"], t["v"], off, off, kc, ki, scale, o=o, ws=ws)
+        if ev is not None:
+            ev[1].record()
+
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    ms, per, events = _timed(stages, step, args.steps, args.warmup)
+    sizes = np.diff(synth.uniform_offsets(cfg.n, cfg.block)).astype(np.int64)
+    kept = int(sizes @ mask.astype(np.int64) @ sizes) * bh
+    flops = 4.0 * cfg.d * kept
+    attn_ms = statistics.mean(events[s][0].elapsed_time(events[s][1]) for s in range(args.steps))
+    attn_tf = flops / (attn_ms * 1e-3) / 1e12
+    dense = None
+    if not args.no_dense:
+        log("[bench] dense attention on the same tensors")
+        od = torch.empty_like(t["q"])
+        sva_full_attn(t["q"], t["k"], t["v"], scale, o=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_reps):
+            sva_full_attn(t["q"], t["k"], t["v"], scale, o=od)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_reps
+        dflops = 4.0 * cfg.d * bh * cfg.n * cfg.n
+        dense = {"ms": dense_ms, "tflops": dflops / (dense_ms * 1e-3) / 1e12,
+                 "frac_of_peak": dflops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "speedup_attention_only": dense_ms / attn_ms}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] fp64 oracle on a bounded sample (host cores)")
+        cpu = cpu_baseline_static(cfg, x, mask)
+    value = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) tokens and a seeded static block mask "
+                "(no dataset)",
+        "config": {"workload": f"static radial + random block mask at {sp:.0%} sparsity, "
+                               f"uniform {cfg.block}-token blocks, attention alone",
+                   "tokens": cfg.n, "grid_thw": [cfg.T, cfg.H, cfg.W], "heads": cfg.heads,
+                   "head_dim": cfg.d, "block": cfg.block, "kept_tiles": int(mask.sum()),
+                   "tiles": int(nb * nb), "sparsity_tiles": round(1 - mask.sum() / nb / nb, 5),
+                   "density": round(kept / float(bh * cfg.n * cfg.n), 5), "kept_pairs": kept},
+        "ms_per_layer": round(ms, 4),
+        "stages_ms_median": {k: round(v_, 4) for k, v_ in per.items()},
+        "attention": {"ms": round(attn_ms, 4), "effective_tflops": round(attn_tf, 2),
+                      "frac_of_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+        "dense": None if dense is None else {k: round(v_, 4) for k, v_ in dense.items()},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def bench_dynamicrad(args) -> int:

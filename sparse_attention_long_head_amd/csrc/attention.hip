@@ -6,14 +6,16 @@
 // block sizes are dynamic, so no tile is padded to a fixed block size.
 //
 // Design (bf16 path):
-// * One workgroup = 4 waves = one tile of up to 128 query rows of one Q block;
-//   each wave owns 32 query rows, held in registers as the B operand of
-//   S^T = K Q^T (32x32x16 bf16 MFMA).  With keys on the accumulator rows and
-//   queries on lanes, every row max / row sum of the online softmax is
-//   in-lane plus one exchange between the two lane halves.
+// * A work item is up to 256 query rows of one Q block; a workgroup of 8 waves
+//   takes it, each wave owning 32 query rows held in registers as the B
+//   operand of S^T = K Q^T (32x32x16 bf16 MFMA).  With keys on the
+//   accumulator rows and queries on lanes, every row max / row sum of the
+//   online softmax is in-lane plus one exchange between the two lane halves.
 // * The kept K blocks of the Q block form one virtual key sequence (their
 //   row ranges concatenated); it is walked in chunks of 64 keys, so a chunk
 //   may span several small clusters and only the very last chunk is partial.
+//   The key row behind each virtual key comes from row-map windows of 16
+//   chunks built by all threads at once in LDS.
 // * A chunk's K and V rows go from HBM straight to LDS (global_load_lds,
 //   16 bytes per lane, no staging registers), row-major with the 16-byte
 //   pieces XOR-swizzled (K and V differently, each for its read pattern);
@@ -21,15 +23,24 @@
 //   operands are conflict-free ds_read_b128 of K; the PV operand V^T comes
 //   from two ds_read_b64_tr_b16 transposing reads, which hand each lane 4
 //   keys of one d in exactly the key order of P^T.
-// * Three LDS buffers per tensor: the copies of chunks c+1 and c+2 are in
-//   flight while chunk c is computed; one partial s_waitcnt + one barrier per
-//   chunk.
+// * Four LDS stages per tensor: chunks c+1 and c+2 are in flight while chunk
+//   c is computed and chunk c-1's V is still read (below); one partial
+//   s_waitcnt + one barrier per chunk.
+// * Ping-pong: the two waves sharing a SIMD (w and w+4) run the same
+//   per-chunk sequence rotated by one phase -- PV(c-1), QK(c), softmax(c)
+//   against softmax(c-1), PV(c-1), QK(c) -- so one is in its MFMA phase while
+//   the other runs VALU work.
 // * Online softmax with a lazy rescale: the running max only moves (and O is
 //   only rescaled) when a row max exceeds it by more than 2^8, so P <= 256.
 //   P is rounded to bf16 for the PV MFMA; max, sum and O accumulate in fp32.
-// * Work items are laid out so consecutive items of a head run on one XCD
-//   (workgroups are dispatched round-robin over the 8 XCDs), keeping a head's
-//   K/V in that XCD's L2.
+// * Sparse mode: one persistent workgroup per compute unit takes items from
+//   per-XCD queues (slices dealt to XCDs by total cost, each XCD working
+//   through its slices one at a time, longest item first within a slice) and
+//   steals from the other queues when its own is empty.  Dense mode: one
+//   workgroup per item, laid out so consecutive items of a head run on one
+//   XCD (workgroups are dispatched round-robin over the 8 XCDs).
+// * Fused permutation (PERM): Q rows, K/V rows and O/LSE rows go through the
+//   permutations, so no permuted copy of any tensor is materialised.
 //
 // The fp32 path is a plain one-thread-per-query kernel (exact fp32, used for
 // small correctness workloads).
