@@ -92,7 +92,7 @@ def main() -> int:
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--workload", default="svg2",
                     choices=["svg2", "static-mask", "static-ratio", "dynamic-threshold",
-                             "kmeans-warm", "sweep"],
+                             "kmeans-warm", "sweep", "adaptive"],
                     help="svg2: k-means clusters + top-p (the default); static-mask: the fixed "
                          "radial + random block mask at --static-sparsity, attention alone; "
                          "static-ratio / "
@@ -140,6 +140,8 @@ def main() -> int:
         return bench_sweep(args)
     if args.workload == "static-mask":
         return bench_static_mask(args)
+    if args.workload == "adaptive":
+        return bench_adaptive(args)
     if args.workload != "svg2":
         return bench_dynamicrad(args)
     cfg = synth.CONFIGS[args.config]
@@ -499,6 +501,68 @@ def bench_static_mask(args) -> int:
                      "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_adaptive(args) -> int:
+    """The layer with a cluster count per head: C_q and C_k chosen per head by
+    choose_clusters (ladders C/2, C, 2C around the clip's counts; the smallest
+    whose k-means objective is within 10% of the objective at the largest),
+    then the layer timed with those counts (heads with equal counts run as one
+    group).  The calibration is outside the timed steps."""
+    import torch
+
+    import synth
+    from sparse_attention_long_head_amd import (AdaptiveSparseVideoAttention, choose_clusters,
+                                                strided_rows)
+
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] adaptive: generating {cfg.name}")
+    x = synth.video_qkv(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv"}
+    del x
+    lq = (cfg.cq // 2, cfg.cq, 2 * cfg.cq)
+    lk = (cfg.ck // 2, cfg.ck, 2 * cfg.ck)
+    t0 = time.perf_counter()
+    cq, rq = choose_clusters(t["q"], lq, iters=5)
+    ck, rk = choose_clusters(t["k"], lk, iters=5)
+    calib_s = time.perf_counter() - t0
+    layer = AdaptiveSparseVideoAttention(cfg.heads, cfg.n, cfg.d, cq, ck, cfg.iters, cfg.top_p,
+                                         device=dev)
+    inits = [(strided_rows(t["q"][:, h0:h1], g.cq), strided_rows(t["k"][:, h0:h1], g.ck))
+             for h0, h1, g in layer.groups]
+    iq, ik = [a for a, _ in inits], [b for _, b in inits]
+    stages = ("layer",)
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        layer(t["q"], t["k"], t["v"], iq, ik)
+        if ev is not None:
+            ev[1].record()
+
+    ms, per, _ = _timed(stages, step, args.steps, args.warmup)
+    kept = layer.kept_pairs()
+    flops = 4.0 * cfg.d * kept
+    value = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded mixture-of-Gaussians video tokens (no dataset)",
+        "config": {"workload": f"svg2 layer with per-head cluster counts, {cfg.name} clip",
+                   "tokens": cfg.n, "heads": cfg.heads, "head_dim": cfg.d,
+                   "ladder_q": list(lq), "ladder_k": list(lk), "cq_per_head": cq,
+                   "ck_per_head": ck, "groups": len(layer.groups),
+                   "density": round(kept / float(cfg.heads * cfg.n * cfg.n), 5),
+                   "calibration_s": round(calib_s, 2)},
+        "objective_over_scatter_q": np.round(rq, 5).tolist(),
+        "objective_over_scatter_k": np.round(rk, 5).tolist(),
+        "ms_per_layer": round(ms, 4),
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
     return 0

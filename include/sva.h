@@ -95,6 +95,26 @@ int32_t sva_kmeans(const void *x, int32_t dtype, int32_t batch, int32_t heads, i
                    int32_t *sizes, int32_t *n_refined, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * sva_cluster_spread -- how tightly a clustering fits each slice, the input of
+ * a per-head choice of the cluster count (Sparse VideoGen2, section 2.b: the
+ * kept density follows the content; the pages give no rule for C itself, so
+ * the caller's rule decides from these two numbers).  Per (b,h) slice, in fp64
+ * with a fixed summation order (deterministic):
+ *   spread[2 bh]     J = sum over rows of ||x - centroids[assign[row]]||^2
+ *                        (the k-means objective)
+ *   spread[2 bh + 1] T = sum over rows of ||x - mean||^2, the slice's scatter
+ *                        (computed as sum ||x||^2 - ||sum x||^2 / n)
+ *
+ *   x          [bh][n][d], dtype SVA_BF16 or SVA_F32
+ *   c          clusters, 1 <= c <= n; centroids [bh][c][d] fp32
+ *   assign     [bh][n] int32 in [0, c) (ids outside are clamped into it)
+ *   spread     [bh][2] fp64 OUT, DEVICE memory owned by the caller
+ * ------------------------------------------------------------------------ */
+int32_t sva_cluster_spread(const void *x, int32_t dtype, int32_t batch, int32_t heads, int32_t n,
+                           int32_t d, int32_t c, const float *centroids, const int32_t *assign,
+                           double *spread, void *stream);
+
+/* ---------------------------------------------------------------------------
  * sva_permute -- semantic-aware permutation (Sparse VideoGen2, section 2.a).
  * A stable counting sort of the rows of each slice by cluster id: clusters in
  * ascending id, rows of a cluster in ascending original index.

@@ -32,6 +32,7 @@ SIGNATURES = {
     "sva_abi_version": (_I, []),
     "sva_kmeans_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "sva_kmeans": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "sva_cluster_spread": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "sva_permute_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "sva_permute": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _Z, _P]),
     "sva_select_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -130,6 +131,18 @@ def sva_kmeans(x: torch.Tensor, c: int, iters: int, centroids: torch.Tensor,
                             _ptr(assign), _ptr(sizes), _ptr(n_refined), _ptr(w), wb, _stream(x)),
            "sva_kmeans")
     return centroids, assign, sizes
+
+
+def sva_cluster_spread(x: torch.Tensor, c: int, centroids: torch.Tensor, assign: torch.Tensor,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per slice (J, T): the k-means objective and the scatter about the mean,
+    fp64 [b, h, 2]."""
+    b, h, n, d = x.shape
+    if out is None:
+        out = torch.empty((b, h, 2), dtype=torch.float64, device=x.device)
+    _check(lib().sva_cluster_spread(_ptr(x), _dtype_code(x), b, h, n, d, c, _ptr(centroids),
+                                    _ptr(assign), _ptr(out), _stream(x)), "sva_cluster_spread")
+    return out
 
 
 def sva_permute(assign: torch.Tensor, c: int, tensors: Sequence[torch.Tensor] = (),

@@ -1859,6 +1859,72 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Spread of a clustering, per slice: J = sum over rows of ||x - c_assign||^2
+// (the k-means objective) and the scatter T = sum over rows of ||x - mean||^2,
+// T taken as sum ||x||^2 - ||sum x||^2 / n.  One workgroup per slice; D/EPT
+// lanes per row (EPT elements each); every lane accumulates its rows in fp64 in
+// ascending order, and lanes, row groups and waves are combined in a fixed
+// order, so the result is deterministic.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void km_spread_kernel(
+    const void *__restrict__ x, int n, int c, const float *__restrict__ cent,
+    const int32_t *__restrict__ assign, double *__restrict__ out) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int EPT = 16 / EB;               // elements per 16-byte piece
+  constexpr int TPR = D / EPT;               // lanes per row
+  constexpr int RPB = kThreads / TPR;        // rows per workgroup pass
+  __shared__ double s_sum[RPB][D];
+  __shared__ double s_jq[kThreads];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int pc = tid % TPR, rg = tid / TPR;
+  const char *xb = static_cast<const char *>(x) + static_cast<size_t>(bh) * n * D * EB;
+  const int32_t *as = assign + static_cast<size_t>(bh) * n;
+  const float *cs = cent + static_cast<size_t>(bh) * c * D;
+  double sx[EPT], j = 0.0, q = 0.0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) sx[e] = 0.0;
+  for (int r = rg; r < n; r += RPB) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(xb + (static_cast<size_t>(r) * D + pc * EPT) * EB);
+    const int a = min(max(as[r], 0), c - 1);
+    const float *cr = cs + static_cast<size_t>(a) * D + pc * EPT;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      float f;
+      if constexpr (BF16) f = bf16_bits_to_f32(static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1))));
+      else f = __uint_as_float(v[e]);
+      const double df = static_cast<double>(f) - static_cast<double>(cr[e]);
+      j = fma(df, df, j);
+      q = fma(static_cast<double>(f), static_cast<double>(f), q);
+      sx[e] += static_cast<double>(f);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) s_sum[rg][pc * EPT + e] = sx[e];
+  s_jq[tid] = j;
+  __syncthreads();
+  // J: fixed-order sum over threads; sum ||x||^2 likewise; ||sum x||^2 from the
+  // row groups' partial sums, added in order per dimension
+  double jt = 0.0, qt = 0.0, s2 = 0.0;
+  if (tid == 0) {
+    for (int t = 0; t < kThreads; ++t) jt += s_jq[t];
+  }
+  __syncthreads();
+  s_jq[tid] = q;
+  __syncthreads();
+  if (tid == 0) {
+    for (int t = 0; t < kThreads; ++t) qt += s_jq[t];
+    for (int dd = 0; dd < D; ++dd) {
+      double col = 0.0;
+      for (int g = 0; g < RPB; ++g) col += s_sum[g][dd];
+      s2 += col * col;
+    }
+    out[2 * bh] = jt;
+    out[2 * bh + 1] = qt - s2 / static_cast<double>(n);
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1914,6 +1980,24 @@ __global__ __launch_bounds__(64) void km_mfma_rounding_kernel(int32_t *__restric
 
 hipError_t launch_mfma_rounding_check(int32_t *flags, hipStream_t s) {
   hipLaunchKernelGGL(km_mfma_rounding_kernel, dim3(1), dim3(64), 0, s, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_spread(const void *x, int32_t dtype, int32_t bh, int32_t n, int32_t d,
+                                 int32_t c, const float *cent, const int32_t *assign,
+                                 double *out, hipStream_t s) {
+#define SVA_SPREAD(DD, B)                                                                     \
+  hipLaunchKernelGGL((km_spread_kernel<DD, B>), dim3(bh), dim3(kThreads), 0, s, x, n, c, cent, \
+                     assign, out)
+  const bool b = dtype == SVA_BF16;
+  if (d == 128) {
+    if (b) SVA_SPREAD(128, true);
+    else SVA_SPREAD(128, false);
+  } else {
+    if (b) SVA_SPREAD(64, true);
+    else SVA_SPREAD(64, false);
+  }
+#undef SVA_SPREAD
   return hipGetLastError();
 }
 

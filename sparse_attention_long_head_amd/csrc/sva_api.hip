@@ -97,6 +97,21 @@ int32_t sva_kmeans(const void *x, int32_t dtype, int32_t batch, int32_t heads, i
   return hip_status(sva::launch_kmeans(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int32_t sva_cluster_spread(const void *x, int32_t dtype, int32_t batch, int32_t heads, int32_t n,
+                           int32_t d, int32_t c, const float *centroids, const int32_t *assign,
+                           double *spread, void *stream) {
+  const char *fn = "sva_cluster_spread";
+  if (!x || !centroids || !assign || !spread)
+    return fail(SVA_EINVAL, "%s: x, centroids, assign and spread must be non-NULL", fn);
+  if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
+  SVA_TRY(check_slices(fn, batch, heads, n));
+  SVA_TRY(check_d(fn, d));
+  if (c < 1 || c > n) return fail(SVA_EINVAL, "%s: need 1 <= c <= n (c=%d, n=%d)", fn, c, n);
+  return hip_status(sva::launch_cluster_spread(x, dtype, batch * heads, n, d, c, centroids, assign,
+                                               spread, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 // ---------------------------------------------------------------------------
 size_t sva_permute_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t c) {
   if (batch < 1 || heads < 1 || n < 1 || c < 1) return 0;

@@ -74,6 +74,9 @@ struct KmeansArgs {
 };
 size_t kmeans_ws_bytes(int32_t bh, int32_t n, int32_t d, int32_t c);
 hipError_t launch_kmeans(const KmeansArgs &a, hipStream_t s);
+hipError_t launch_cluster_spread(const void *x, int32_t dtype, int32_t bh, int32_t n, int32_t d,
+                                 int32_t c, const float *cent, const int32_t *assign,
+                                 double *out, hipStream_t s);
 
 // stable counting sort of rows by cluster id (shared by k-means and permute);
 // `clear`, if not NULL, holds bh ints that the sort sets to zero; `seg`, if

@@ -34,7 +34,7 @@ class SparseVideoAttention:
                  top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda",
                  scale: Optional[float] = None, want_lse: bool = False,
                  fuse_permutation: bool = True, theta: Optional[float] = None,
-                 iters_warm: Optional[int] = None):
+                 iters_warm: Optional[int] = None, out: Optional[torch.Tensor] = None):
         self.shape = (batch, heads, n, d)
         # centroid cache (Sparse VideoGen2, section 2.c): a call without
         # initial centroids starts from the previous call's final ones and runs
@@ -69,7 +69,14 @@ class SparseVideoAttention:
         self.mask = torch.empty((batch, heads, cq, ck), dtype=torch.uint8, device=dev)
         self.kept_count = torch.empty((batch, heads, cq), **i32)
         self.kept_idx = torch.empty((batch, heads, cq, ck), **i32)
-        self.o = torch.empty(self.shape, dtype=dtype, device=dev)
+        # the output: a caller-provided contiguous buffer (e.g. a head range of a
+        # larger output) or one of our own
+        if out is not None:
+            if tuple(out.shape) != self.shape or not out.is_contiguous() or out.dtype != dtype:
+                raise ValueError("out must be a contiguous tensor of the layer's shape and dtype")
+            self.o = out
+        else:
+            self.o = torch.empty(self.shape, dtype=dtype, device=dev)
         # LSE per query row: in original token order when fused, else of the
         # permuted rows (row i belongs to token perm_q[i])
         self.lse = torch.empty((batch, heads, n), **f32) if want_lse else None
@@ -258,3 +265,81 @@ class RadialSparseAttention:
         sizes = (self.off[0, 0, 1:] - self.off[0, 0, :-1]).cpu().numpy().astype(np.int64)
         m = self.mask.cpu().numpy().astype(np.int64)
         return int(np.einsum("i,bhij,j->", sizes, m, sizes))
+
+
+def strided_rows(x: torch.Tensor, c: int) -> torch.Tensor:
+    """Initial centroids for a calibration run: rows floor(i * n / c) of every
+    slice of x [b, h, n, d], as fp32 [b, h, c, d] (no random numbers, so a
+    calibration is reproducible)."""
+    n = x.shape[2]
+    idx = (torch.arange(c, device=x.device, dtype=torch.int64) * n) // c
+    return x[:, :, idx, :].float().contiguous()
+
+
+def choose_clusters(x: torch.Tensor, ladder, iters: int, delta: float = 0.1):
+    """Per-head cluster count: the smallest C of ``ladder`` whose k-means
+    objective J(C) is within (1 + delta) of the objective at the largest C
+    (the point past which more clusters stop fitting the content better).
+    Each candidate runs ``iters`` Lloyd iterations from strided rows; the
+    objectives come from sva_cluster_spread.  Returns (list of C per head,
+    [len(ladder), heads] array of J / T, T being each head's scatter).  Batch 1."""
+    ladder = sorted(int(c) for c in ladder)
+    b, h, n, d = x.shape
+    if b != 1:
+        raise ValueError("choose_clusters: batch 1 only")
+    dev = x.device
+    J = np.zeros((len(ladder), h))
+    T = np.zeros(h)
+    assign = torch.empty((b, h, n), dtype=torch.int32, device=dev)
+    for i, c in enumerate(ladder):
+        cent = strided_rows(x, c)
+        sizes = torch.empty((b, h, c), dtype=torch.int32, device=dev)
+        L.sva_kmeans(x, c, iters, cent, assign, sizes)
+        sp = L.sva_cluster_spread(x, c, cent, assign).cpu().numpy()[0]
+        J[i] = sp[:, 0]
+        T = sp[:, 1]
+    chosen = []
+    for j in range(h):
+        ok = [i for i in range(len(ladder)) if J[i, j] <= (1.0 + delta) * J[-1, j]]
+        chosen.append(ladder[ok[0]])
+    return chosen, J / np.maximum(T, 1e-300)[None, :]
+
+
+class AdaptiveSparseVideoAttention:
+    """The SVG2 layer with its own (C_q, C_k) per head: consecutive heads with
+    equal counts form a group that runs as one ``SparseVideoAttention`` on its
+    head range, writing straight into that range of one output tensor.  Batch 1
+    (a head range of a [1, H, n, d] tensor is contiguous)."""
+
+    def __init__(self, heads: int, n: int, d: int, cq_per_head, ck_per_head, iters: int,
+                 top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda", **kw):
+        cq_per_head, ck_per_head = list(cq_per_head), list(ck_per_head)
+        if len(cq_per_head) != heads or len(ck_per_head) != heads:
+            raise ValueError("one C_q and one C_k per head")
+        dev = torch.device(device)
+        self.o = torch.empty((1, heads, n, d), dtype=dtype, device=dev)
+        self.groups = []          # (h0, h1, layer)
+        h0 = 0
+        while h0 < heads:
+            h1 = h0 + 1
+            while h1 < heads and (cq_per_head[h1], ck_per_head[h1]) == (cq_per_head[h0],
+                                                                      ck_per_head[h0]):
+                h1 += 1
+            layer = SparseVideoAttention(1, h1 - h0, n, d, cq_per_head[h0], ck_per_head[h0],
+                                         iters, top_p, dtype=dtype, device=dev,
+                                         out=self.o[:, h0:h1], **kw)
+            self.groups.append((h0, h1, layer))
+            h0 = h1
+
+    def forward(self, q, k, v, init_q=None, init_k=None) -> torch.Tensor:
+        """init_q / init_k: one initial-centroid tensor per group ([1, g, C, d]),
+        or None for a warm start from the previous call."""
+        for gi, (h0, h1, layer) in enumerate(self.groups):
+            layer(q[:, h0:h1], k[:, h0:h1], v[:, h0:h1],
+                  None if init_q is None else init_q[gi], None if init_k is None else init_k[gi])
+        return self.o
+
+    __call__ = forward
+
+    def kept_pairs(self) -> int:
+        return sum(layer.kept_pairs() for _, _, layer in self.groups)

@@ -68,6 +68,19 @@ def test_kmeans_validation(L):
         assert L.last_error().startswith("sva_kmeans")
 
 
+def test_cluster_spread_validation(L):
+    lib = L.lib()
+    ok = [P, 1, 1, 2, 1000, 128, 10, P, P, P, None]
+    for i, bad, want in [(0, None, L.SVA_EINVAL), (1, 9, L.SVA_EINVAL), (4, 0, L.SVA_EINVAL),
+                         (5, 96, L.SVA_EUNSUPPORTED), (6, 0, L.SVA_EINVAL),
+                         (6, 1001, L.SVA_EINVAL), (7, None, L.SVA_EINVAL),
+                         (8, None, L.SVA_EINVAL), (9, None, L.SVA_EINVAL)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.sva_cluster_spread(*args) == want, (i, bad)
+    assert L.last_error().startswith("sva_cluster_spread")
+
+
 def test_permute_validation(L):
     lib = L.lib()
     ws = lib.sva_permute_workspace_bytes(1, 1, 100, 7)
