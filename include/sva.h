@@ -260,6 +260,27 @@ int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32
                               float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * sva_block_sparse_attn_noalloc -- sva_block_sparse_attn for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): no workspace argument; the work
+ * schedule lives in a static device array of 8 MiB per GPU, held by the
+ * library until the process ends.  The call allocates and frees nothing.
+ * Arguments, results and errors are those of sva_block_sparse_attn, plus:
+ *   SVA_EWORKSPACE  the schedule (sva_attn_workspace_bytes(batch, heads, n_q,
+ *                   n_qblocks)) exceeds 8 MiB; nothing is launched
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (different streams, different threads) race and must be ordered by the
+ * caller.  Each call rewrites every part of the array it reads.
+ * ------------------------------------------------------------------------ */
+int32_t sva_block_sparse_attn_noalloc(const void *q, const void *k, const void *v,
+                                      int32_t dtype, int32_t batch, int32_t heads, int32_t n_q,
+                                      int32_t n_k, int32_t d, const int32_t *q_offsets,
+                                      int32_t n_qblocks, const int32_t *k_offsets,
+                                      int32_t n_kblocks, const int32_t *kept_count,
+                                      const int32_t *kept_idx, int32_t kept_stride, float scale,
+                                      void *o, int32_t o_dtype, float *lse, void *stream);
+
+/* ------------------------------------------------------------------------
  * sva_block_sparse_attn_perm -- the same attention with the permutation
  * fused into its loads and stores (Sparse VideoGen2, section 2.a: the
  * permutation only makes each cluster contiguous; section 2.c: sparse loading

@@ -45,6 +45,8 @@ SIGNATURES = {
     "sva_attn_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "sva_block_sparse_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P,
                                    _I, _F, _P, _I, _P, _P, _Z, _P]),
+    "sva_block_sparse_attn_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _I,
+                                           _P, _P, _I, _F, _P, _I, _P, _P]),
     "sva_block_sparse_attn_perm": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P,
                                         _I, _P, _P, _I, _F, _P, _I, _P, _P, _Z, _P]),
     "sva_unpermute": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
@@ -276,6 +278,24 @@ def sva_block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                        _ptr(kept_count), _ptr(kept_idx), kept_idx.shape[-1],
                                        float(scale), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(w),
                                        wb, _stream(q)), "sva_block_sparse_attn")
+    return o, lse
+
+
+def sva_block_sparse_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  q_offsets: torch.Tensor, k_offsets: torch.Tensor,
+                                  kept_count: torch.Tensor, kept_idx: torch.Tensor, scale: float,
+                                  o: torch.Tensor, lse: Optional[torch.Tensor] = None):
+    """sva_block_sparse_attn with the library's static schedule scratch: the
+    caller provides o (and lse, optional); nothing is allocated."""
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    _check(lib().sva_block_sparse_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), b, h,
+                                               nq, nk, d, _ptr(q_offsets),
+                                               q_offsets.shape[-1] - 1, _ptr(k_offsets),
+                                               k_offsets.shape[-1] - 1, _ptr(kept_count),
+                                               _ptr(kept_idx), kept_idx.shape[-1], float(scale),
+                                               _ptr(o), _dtype_code(o), _ptr(lse), _stream(q)),
+           "sva_block_sparse_attn_noalloc")
     return o, lse
 
 

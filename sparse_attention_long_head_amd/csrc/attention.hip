@@ -47,6 +47,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/sva.h"
@@ -956,6 +957,39 @@ int device_cus() {
 
 size_t attn_ws_bytes(int32_t bh, int32_t n_q, int32_t nqb) {
   return sched_layout(bh, n_q, nqb).total;
+}
+
+// ---------------------------------------------------------------------------
+// Static schedule scratch of the no-allocation attention entry point: one
+// array per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it only stands in for
+// the symbol); its device address is looked up once per device, with that
+// device current, and kept.  Every call on a GPU shares that GPU's array, so
+// calls that overlap on one GPU race; the schedule kernels rewrite every part
+// of it they read (items, costs, queues and their counters) on each call.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticAttnScratch];
+
+void *attn_static_scratch(hipError_t *err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *ptr[kMaxDevices] = {};
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void *p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptr[dev];
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {

@@ -267,7 +267,8 @@ static int32_t block_sparse(const char *fn, const void *q, const void *k, const 
                             const int32_t *k_offsets, int32_t n_kblocks,
                             const int32_t *kept_count, const int32_t *kept_idx,
                             int32_t kept_stride, float scale, void *o, int32_t o_dtype,
-                            float *lse, void *ws, size_t ws_bytes, void *stream) {
+                            float *lse, void *ws, size_t ws_bytes, void *stream,
+                            bool static_ws = false) {
   SVA_TRY(check_attn(fn, q, k, v, dtype, batch, heads, n_q, n_k, d, scale, o, o_dtype));
   if (!q_offsets || !k_offsets || !kept_count || !kept_idx)
     return fail(SVA_EINVAL, "%s: offsets and kept lists must be non-NULL", fn);
@@ -278,7 +279,20 @@ static int32_t block_sparse(const char *fn, const void *q, const void *k, const 
   if (kept_stride < 1) return fail(SVA_EINVAL, "%s: kept_stride must be >= 1", fn);
   const long long items = static_cast<long long>(batch) * heads * ((n_q + 127) / 128 + n_qblocks);
   if (items > 0x7ffffff0LL) return fail(SVA_EUNSUPPORTED, "%s: problem too large for one launch", fn);
-  SVA_TRY(check_ws(fn, sva::attn_ws_bytes(batch * heads, n_q, n_qblocks), ws, ws_bytes));
+  const size_t need = sva::attn_ws_bytes(batch * heads, n_q, n_qblocks);
+  if (static_ws) {
+    if (need > sva::kStaticAttnScratch)
+      return fail(SVA_EWORKSPACE,
+                  "%s: the work schedule needs %zu bytes, more than the %zu-byte static scratch "
+                  "(use sva_block_sparse_attn with a workspace)",
+                  fn, need, sva::kStaticAttnScratch);
+    hipError_t e = hipSuccess;
+    ws = sva::attn_static_scratch(&e);
+    if (ws == nullptr) return hip_status(e, fn);
+    ws_bytes = sva::kStaticAttnScratch;
+  } else {
+    SVA_TRY(check_ws(fn, need, ws, ws_bytes));
+  }
   sva::AttnArgs a{q, k, v, o, lse, q_offsets, k_offsets, kept_count, kept_idx, q_perm, k_perm,
                   kept_stride, batch * heads, n_q, n_k, d, n_qblocks, n_kblocks, dtype, o_dtype,
                   0, scale, ws};
@@ -295,6 +309,18 @@ int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32
   return block_sparse("sva_block_sparse_attn", q, k, v, dtype, batch, heads, n_q, n_k, d,
                       nullptr, nullptr, q_offsets, n_qblocks, k_offsets, n_kblocks, kept_count,
                       kept_idx, kept_stride, scale, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int32_t sva_block_sparse_attn_noalloc(const void *q, const void *k, const void *v,
+                                      int32_t dtype, int32_t batch, int32_t heads, int32_t n_q,
+                                      int32_t n_k, int32_t d, const int32_t *q_offsets,
+                                      int32_t n_qblocks, const int32_t *k_offsets,
+                                      int32_t n_kblocks, const int32_t *kept_count,
+                                      const int32_t *kept_idx, int32_t kept_stride, float scale,
+                                      void *o, int32_t o_dtype, float *lse, void *stream) {
+  return block_sparse("sva_block_sparse_attn_noalloc", q, k, v, dtype, batch, heads, n_q, n_k, d,
+                      nullptr, nullptr, q_offsets, n_qblocks, k_offsets, n_kblocks, kept_count,
+                      kept_idx, kept_stride, scale, o, o_dtype, lse, nullptr, 0, stream, true);
 }
 
 int32_t sva_block_sparse_attn_perm(const void *q, const void *k, const void *v, int32_t dtype,

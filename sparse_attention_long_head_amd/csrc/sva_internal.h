@@ -64,6 +64,10 @@ struct AttnArgs {
 };
 size_t attn_ws_bytes(int32_t bh, int32_t n_q, int32_t nqb);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+// the static schedule scratch of the no-allocation entry point: its device
+// address on the current device (looked up once per device), or NULL with *err
+constexpr size_t kStaticAttnScratch = size_t{8} << 20;
+void *attn_static_scratch(hipError_t *err);
 
 struct KmeansArgs {
   const void *x;

@@ -184,3 +184,17 @@ def test_valid_call_without_gpu_returns_hip_error(L):
     assert lib.sva_full_attn(P, P, P, 1, 1, 2, 100, 100, 128, 0.088, P, 1, None, P, ws,
                              None) == L.SVA_EHIP
     assert L.last_error().startswith("sva_full_attn")
+
+
+def test_noalloc_attention_rejects_a_schedule_beyond_its_scratch(L):
+    """The static-scratch entry point refuses a schedule larger than its 8 MiB
+    before any HIP call (so this runs without a GPU)."""
+    lib = L.lib()
+    need = lib.sva_attn_workspace_bytes(1, 4096, 32760, 256)
+    assert need > 8 << 20
+    st = lib.sva_block_sparse_attn_noalloc(P, P, P, 1, 1, 4096, 32760, 32760, 128, P, 256, P, 256,
+                                           P, P, 256, 0.088, P, 1, None, None)
+    assert st == L.SVA_EWORKSPACE
+    assert "static scratch" in L.last_error()
+    assert lib.sva_block_sparse_attn_noalloc(P, P, P, 1, 1, 2, 1000, 1000, 128, P, 8, P, 0, P, P,
+                                             8, 0.088, P, 1, None, None) == L.SVA_EINVAL
