@@ -75,8 +75,8 @@ constexpr int kCandTok = 32 * kCandWaves;       // sorted positions per workgrou
 constexpr int kNbrMaxC = 4096;                  // largest C of the candidate path
 
 struct KmLayout {
-  size_t chi, clo, nh, ctl, flags, tflags, qids, tcount, pcount, perm, seg, offsets, rad, nbr,
-      tun, sort, total;
+  size_t chi, clo, nh, ctl, flags, tflags, tcount, pcount, perm, seg, offsets, rad, nbr, tun,
+      sort, total;
 };
 
 // ctl holds the bh refine-queue lengths
@@ -95,7 +95,6 @@ KmLayout km_layout(int32_t bh, int32_t n, int32_t d, int32_t c) {
   L.ctl = take(static_cast<size_t>(bh) * 4);
   L.flags = take(static_cast<size_t>(bh) * n * 8);
   L.tflags = take(static_cast<size_t>(bh) * n * 8);
-  L.qids = take(static_cast<size_t>(bh) * n * 8);     // candidate ids of queued rows
   L.tcount = take(static_cast<size_t>(bh) * ((n + kResTok - 1) / kResTok) * 4);   // any pass
   L.pcount = take(static_cast<size_t>(bh) * ((n + kCandTok - 1) / kCandTok) * 4);
   L.perm = take(static_cast<size_t>(bh) * n * 4);
@@ -968,8 +967,8 @@ __global__ __launch_bounds__(kThreads) void km_queue_join_kernel(
 //                       iteration's sorted order, the OR of the rows of the
 //                       tile's clusters (a run of ids, since the order is
 //                       sorted by cluster)
-//   km_assign_cand_kernel  the tile's tokens against the clusters of its union
-//   km_settle_kernel    the rows it left undecided, in fp64, over the union
+//   km_assign_cand_kernel  the tile's tokens against the clusters of its union,
+//                       then the rows the fast path leaves undecided, in fp64
 // ---------------------------------------------------------------------------
 
 // Neighbour bits.  A workgroup takes kNbrWaves tiles of 32 clusters a of a
@@ -1156,9 +1155,9 @@ template <int D>
 __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
     const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
     const uint16_t *__restrict__ clo, const float *__restrict__ nh,
-    const int32_t *__restrict__ perm, const uint32_t *__restrict__ tun,
-    int32_t *__restrict__ assign, int2 *__restrict__ tflags, uint64_t *__restrict__ qids,
-    int32_t *__restrict__ tcount, int32_t *__restrict__ pcount, int nbh, int tph) {
+    const float *__restrict__ cent, const int32_t *__restrict__ perm,
+    const uint32_t *__restrict__ tun, int32_t *__restrict__ assign,
+    int32_t *__restrict__ n_refined, int nbh, int tph) {
   constexpr int NS = D / 16;
   constexpr int kThr = 64 * kCandWaves;
   constexpr int PPR = D / 8;                        // 16-byte pieces per row
@@ -1173,6 +1172,8 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
   __shared__ int32_t sU[kUnionCap];
   __shared__ int32_t s_wsum[kCandWaves];
   __shared__ int32_t s_wq[kCandWaves], s_wp[kCandWaves];
+  __shared__ int2 sRow[kCandTok];             // undecided rows: queued first, pairs last
+  __shared__ uint64_t sQid[kCandTok];         // listed candidate ids of queued rows
   const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
   const int bh = xcd + 8 * (k8 / tph);
   const int tile = k8 % tph;
@@ -1360,101 +1361,56 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
         listed |= static_cast<uint64_t>(uid(vv * 32 + __builtin_ctz(m))) << (16 * nlisted);
   }
   const uint64_t qm = __ballot(queued), pmk = __ballot(paired);
-  const uint64_t wm = __ballot(queued && nlisted == 0);
   if (lane == 0) {
-    s_wq[wave] = __popcll(qm) | (__popcll(wm) << 16);
+    s_wq[wave] = __popcll(qm);
     s_wp[wave] = __popcll(pmk);
   }
   __syncthreads();
-  // s_wq: queued rows of the wave (bits 0-15) and those without listed ids
-  // (bits 16-31); the tile's count keeps the same layout
-  int q = base, pp = 0, tot = 0, ptot = 0, wide = 0;
+  int q = 0, pp = 0, nq = 0, np = 0;
 #pragma unroll
   for (int w = 0; w < kCandWaves; ++w) {
-    q += w < wave ? (s_wq[w] & 0xffff) : 0;
+    q += w < wave ? s_wq[w] : 0;
     pp += w < wave ? s_wp[w] : 0;
-    tot += s_wq[w] & 0xffff;
-    wide += s_wq[w] >> 16;
-    ptot += s_wp[w];
+    nq += s_wq[w];
+    np += s_wp[w];
   }
   const uint64_t lt = (1ull << lane) - 1;
   if (queued) {
-    const size_t at = static_cast<size_t>(bh) * n + q + __popcll(qm & lt);
-    tflags[at] = int2{tok, nlisted};
-    qids[at] = listed;
+    const int at = q + __popcll(qm & lt);
+    sRow[at] = int2{tok, nlisted};
+    sQid[at] = listed;
   }
-  if (paired)
-    tflags[static_cast<size_t>(bh) * n + last - (pp + __popcll(pmk & lt))] =
-        int2{tok, (ival << 16) | ival2};
-  if (tid == 0) {
-    tcount[static_cast<size_t>(bh) * tph + tile] = tot | (wide << 16);
-    pcount[static_cast<size_t>(bh) * tph + tile] = ptot;
-  }
-}
+  if (paired) sRow[kCandTok - 1 - (pp + __popcll(pmk & lt))] = int2{tok, (ival << 16) | ival2};
+  __syncthreads();
 
-// Settle the rows the candidate pass left undecided, exactly, in fp64: a pair
-// row compares its two clusters, a queued row the (up to four) clusters the
-// assign pass listed for it, or, when it listed none, every cluster of the
-// tile's union (a superset of the row's own candidates).  One workgroup per
-// token tile; a group of 8 lanes per row (D/8 dimensions per lane, each lane's
-// terms added in ascending order, the lanes in a fixed butterfly), four
-// candidates loaded at a time; the smallest distance wins, ties to the lowest
-// id.
-template <int D>
-__global__ __launch_bounds__(kThreads) void km_settle_kernel(
-    const uint16_t *__restrict__ x, int n, int c, int cpad, const float *__restrict__ cent,
-    const uint32_t *__restrict__ tun, const int2 *__restrict__ tflags,
-    const uint64_t *__restrict__ qids, const int32_t *__restrict__ tcount,
-    const int32_t *__restrict__ pcount, int32_t *__restrict__ assign,
-    int32_t *__restrict__ n_refined, int nbh, int tph) {
+  // Settle the undecided rows exactly, in fp64: a pair row compares its two
+  // clusters, a queued row the (up to four) clusters listed for it, or, when
+  // none were listed, every cluster of the union.  A group of 8 lanes per row
+  // (D/8 dimensions per lane, each lane's terms added in ascending order, the
+  // lanes in a fixed butterfly), four candidates loaded at a time; the
+  // smallest distance wins, ties to the lowest id.
   constexpr int LPR = 8;                     // lanes per row
   constexpr int DPL = D / LPR;               // dimensions per lane (8 or 16)
   constexpr int XQ = DPL / 8;                // 16-byte pieces of x per lane
   constexpr int CQ = 2 * XQ;                 // 16-byte pieces of a centroid per lane
-  constexpr int GPB = kThreads / LPR;        // rows in flight per workgroup
+  constexpr int GPB = kThr / LPR;            // rows in flight per workgroup
   constexpr int U = 4;                       // candidates loaded at a time
-  __shared__ int32_t sU[kUnionCap];
-  __shared__ int32_t s_wsum[kThreads / 64];
-  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
-  const int bh = xcd + 8 * (k8 / tph);
-  const int tile = k8 % tph;
-  if (bh >= nbh) return;
-  const int tq = tcount[static_cast<size_t>(bh) * tph + tile];
-  const int nq = tq & 0xffff, nwide = tq >> 16;
-  const int np = pcount[static_cast<size_t>(bh) * tph + tile];
-  if (nq + np == 0) return;                  // uniform
-  const int tid = threadIdx.x, sub = tid % LPR, grp = tid / LPR;
-  const int base = tile * kCandTok;
-  const int last = base + min(kCandTok, n - base) - 1;
-  const int nw = cpad / 32;
-  const uint16_t *xb = x + static_cast<size_t>(bh) * n * D;
+  const int sub = tid % LPR, grp = tid / LPR;
   const float *cs = cent + static_cast<size_t>(bh) * c * D;
-  int32_t *as = assign + static_cast<size_t>(bh) * n;
-  int nu = c;
-  bool all = true;
-  if (nwide > 0) {                           // uniform
-    const uint32_t m_own =
-        tid < nw ? tun[(static_cast<size_t>(bh) * tph + tile) * nw + tid] : 0u;
-    nu = tile_union_ids<kThreads>(m_own, sU, kUnionCap, s_wsum);
-    all = nu > kUnionCap || nu >= c;
-    if (all) nu = c;
-  }
   for (int k = grp; k < nq + np; k += GPB) {   // uniform over the row's lanes
     const bool pair = k >= nq;
-    const size_t at = static_cast<size_t>(bh) * n + (pair ? last - (k - nq) : base + k);
-    const int2 e = tflags[at];
-    const uint64_t li = pair ? 0ull : qids[at];
+    const int2 e = pair ? sRow[kCandTok - 1 - (k - nq)] : sRow[k];
+    const uint64_t li = pair ? 0ull : sQid[k];
     u32x4 xv[XQ];
 #pragma unroll
     for (int i = 0; i < XQ; ++i)
       xv[i] = reinterpret_cast<const u32x4 *>(xb + static_cast<size_t>(e.x) * D)[sub * XQ + i];
-    // candidate j of this row: the pair's two, the listed ids, or the union
     const int cnt = pair ? 2 : (e.y > 0 ? e.y : nu);
     auto cand_id = [&](int j) {
       if (j >= cnt) return -1;
       if (pair) return j == 0 ? (e.y >> 16) & 0xffff : e.y & 0xffff;
       if (e.y > 0) return static_cast<int>((li >> (16 * j)) & 0xffff);
-      return all ? j : sU[j];
+      return uid(j);
     };
     double bd = INFINITY;
     int bi = 0x7fffffff;
@@ -1488,7 +1444,7 @@ __global__ __launch_bounds__(kThreads) void km_settle_kernel(
     }
     if (sub == 0) as[e.x] = bi;
   }
-  if (n_refined != nullptr && tid == 0) atomicAdd(n_refined, nq + np);
+  if (n_refined != nullptr && tid == 0 && nq + np > 0) atomicAdd(n_refined, nq + np);
 }
 
 // ---------------------------------------------------------------------------
@@ -1722,7 +1678,6 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
   int32_t *ctl = reinterpret_cast<int32_t *>(w + L.ctl);   // [bh] refine-queue lengths
   int2 *flags = reinterpret_cast<int2 *>(w + L.flags);
   int2 *tflags = reinterpret_cast<int2 *>(w + L.tflags);
-  uint64_t *qids = reinterpret_cast<uint64_t *>(w + L.qids);
   int32_t *tcount = reinterpret_cast<int32_t *>(w + L.tcount);
   int32_t *pcount = reinterpret_cast<int32_t *>(w + L.pcount);
   int32_t *perm = reinterpret_cast<int32_t *>(w + L.perm);
@@ -1794,12 +1749,8 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
                          a.c, cpad, ctph, tun);
       SVA_CHECK(hipGetLastError());
       hipLaunchKernelGGL((km_assign_cand_kernel<D>), cand_grid, dim3(64 * kCandWaves), 0, s,
-                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh, perm,
-                         tun, a.assign, tflags, qids, tcount, pcount, a.bh, ctph);
-      SVA_CHECK(hipGetLastError());
-      hipLaunchKernelGGL((km_settle_kernel<D>), cand_grid, dim3(kThreads), 0, s,
-                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, a.centroids, tun,
-                         tflags, qids, tcount, pcount, a.assign, a.n_refined, a.bh, ctph);
+                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
+                         a.centroids, perm, tun, a.assign, a.n_refined, a.bh, ctph);
       SVA_CHECK(hipGetLastError());
     } else if (bf16) {
       // the pair path (third best tracked) pays once the refine's re-scan is
