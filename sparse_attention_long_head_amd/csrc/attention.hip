@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void attn_cost_kernel(
 
 __global__ __launch_bounds__(kThreads) void attn_schedule_kernel(
     const int32_t *__restrict__ q_off, const int32_t *__restrict__ qcost, int nqb,
-    int work_cap, WorkItem *__restrict__ work, int32_t *__restrict__ hinfo) {
+    int work_cap, int split, WorkItem *__restrict__ work, int32_t *__restrict__ hinfo) {
   __shared__ int32_t wsum[4];
   __shared__ int32_t csum[4];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -233,12 +233,19 @@ __global__ __launch_bounds__(kThreads) void attn_schedule_kernel(
   int base = 0, cost_sum = 0;
   for (int b0 = 0; b0 < nqb; b0 += kThreads) {
     const int qb = b0 + t;
-    int tiles = 0, cost = 0;
+    int tiles = 0, cost = 0, rows = 0;
     if (qb < nqb) {
-      tiles = max(0, (off[qb + 1] - off[qb] + kQTile - 1) / kQTile);
+      rows = max(0, off[qb + 1] - off[qb]);
+      tiles = (rows + kQTile - 1) / kQTile;
       cost = qcost[static_cast<size_t>(bh) * nqb + qb];
     }
-    int x = tiles, cs = tiles * cost;
+    // (split mode) a last item of at most half a tile takes about half the
+    // chunk time
+    const int rem = rows - (tiles - 1) * kQTile;
+    const int cost_last = split && tiles > 0 && rem <= kQTile / 2
+                              ? (cost - kItemFixed + 1) / 2 + kItemFixed
+                              : cost;
+    int x = tiles, cs = tiles > 0 ? (tiles - 1) * cost + cost_last : 0;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o);
@@ -257,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void attn_schedule_kernel(
     }
     const int first = base + pre + x - tiles;
     for (int i = 0; i < tiles; ++i)
-      if (first + i < work_cap) out[first + i] = WorkItem{bh, qb, i * kQTile, cost};
+      if (first + i < work_cap)
+        out[first + i] = WorkItem{bh, qb, i * kQTile, i == tiles - 1 ? cost_last : cost};
     base += total;
     __syncthreads();
   }
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention
 // ---------------------------------------------------------------------------
-template <int D, bool OUT_F32, bool PERM, int W>
+template <int D, bool OUT_F32, bool PERM, int W, bool SPLIT>
 __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, void *__restrict__ o, float *__restrict__ lse,
@@ -415,7 +423,18 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
   auto item = [&](const int bh, const int qb, const int row0) {
   const int qs = dense ? 0 : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb];
   const int qe = dense ? n_q : q_off[static_cast<size_t>(bh) * (nqb + 1) + qb + 1];
-  const int rbase = qs + row0 + wave * kWaveRows;
+  // Split mode (an item of at most half the tile's rows, one 32-row query
+  // tile per wave pair): the two waves that share a SIMD, w and w + W/2, take
+  // the same query rows, wave w the first 32 keys of every chunk and wave
+  // w + W/2 the last 32; their partial softmax states are merged at the end.
+  // Each step's work per wave is then halved, so such an item runs in less
+  // time than a full one instead of leaving half the waves idle.  The wave's
+  // K and V fragment addresses move to its key half for the item.  (SPLIT:
+  // the instantiation for Q blocks of at most kQTile / 2 rows on average; the
+  // other one has none of this code, which keeps its full-item schedule.)
+  const bool split = SPLIT && NT == 1 && qe - (qs + row0) <= kQTile / 2;   // uniform
+  const int mt_own = split ? wave / (W / 2) : 0;                   // split: own key half
+  const int rbase = qs + row0 + (split ? wave % (W / 2) : wave) * kWaveRows;
   const bool wave_active = rbase < qe;
   bool nt_active[NT];
   int myq[NT];
@@ -495,6 +514,11 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
   for (int dt = 0; dt < ND; ++dt)
     va[dt] = sv0 + tr_row * D * 2 + ((((dt << 2) | tr_c0) ^ tr_x) << 4) + tr_in * 2;
 
+  const uint32_t split_off = static_cast<uint32_t>(mt_own) * 32 * D * 2;   // LDS bytes
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ka[s] += split_off;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) va[dt] += split_off;
   for (int seg0 = 0; seg0 < kc; seg0 += kLCap) {
     // the segment's kept clusters as key-row ranges, empty ones dropped:
     // sStart[j] = first row, sCum[j] = virtual index of that row (exclusive scan)
@@ -648,6 +672,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       constexpr int ST = decltype(st)::value;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
+        if (mt == 1 && split) break;   // split: one m-tile, the wave's key half
         bf16x8 kf[NS];
         if (mt == 0) lds_read_frags<ST * kStageBytes>(kf, ka);
         else lds_read_frags<ST * kStageBytes + 32 * D * 2>(kf, ka);
@@ -664,24 +689,30 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     // online softmax of chunk cc: scores in sacc -> bf16 probabilities in pb,
     // running max / sum updated, O rescaled when the max grows by > 2^kLazy
     auto softmax = [&](int cc) {
+      const int k0 = cc * kKT + mt_own * 32;   // key of m-tile 0, row 0
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (!nt_active[nt]) continue;
+        // (split: only m-tile 0 holds scores)
         if ((cc + 1) * kKT > L) {     // partial last chunk: mask keys past the end
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < 2; ++mt) {
+            if (mt == 1 && split) break;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (cc * kKT + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
+              if (k0 + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
+          }
         }
         // (maximum, not maxnum: no NaN canonicalisation, so v_maximum3 does 2 per
         // op); four independent chains keep the reduction short
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+          if (mt == 1 && split) break;
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             m4[i & 3] = __builtin_elementwise_maximum(m4[i & 3], sacc[nt][mt][i]);
+        }
         float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]),
                                                  __builtin_elementwise_maximum(m4[2], m4[3]));
         {   // both lane halves hold the same query: exchange with permlane32_swap
@@ -700,15 +731,21 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
             for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
           m_run[nt] = m_new;
         }
+        // (split: a key half may hold no key at all, the tail of the last
+        // chunk; while the wave has seen no key its max stays -inf and the
+        // exponent is taken against 0, giving p = 0)
+        const float m_sub = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
         float ps[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+          if (mt == 1 && split) break;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_run[nt]));
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_sub));
             ps[i & 3] += p;
             pb[nt][2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
           }
+        }
         l_run[nt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       }
     };
@@ -719,6 +756,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       if constexpr (ND == 4) {   // two k-steps per LDS round trip
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
+          if (kp == 1 && split) break;   // split: the wave's 32 keys only
           bf16x8 vf[2][ND];
           if (kp == 0)
             lds_read_vt2<ST * kStageBytes, ST * kStageBytes + 16 * D * 2, 8 * D * 2>(vf[0], vf[1], va);
@@ -737,6 +775,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+          if (ks == 2 && split) break;   // split: the wave's 32 keys only
           bf16x8 vf[ND];
           if (ks == 0) lds_read_vt<ST * kStageBytes, 8 * D * 2>(vf, va);
           else if (ks == 1) lds_read_vt<ST * kStageBytes + 16 * D * 2, 8 * D * 2>(vf, va);
@@ -792,13 +831,57 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     wait_vmcnt<0>();   // the copies past the end must land before the stages are reused
     lds_barrier();     // the next segment reuses the LDS buffers and lists
   }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ka[s] -= split_off;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) va[dt] -= split_off;
+
+  // split mode: wave w + W/2 hands its (max, sum, O) to wave w through LDS
+  // (the K/V stages are free now), which merges them into its own
+  if (split) {
+    f32x4 *sO = reinterpret_cast<f32x4 *>(&sK[0][0]);      // [W/2][ND*4][64]
+    float *sM = reinterpret_cast<float *>(&sV[0][0]);      // [W/2][2][64]
+    const int pw = wave % (W / 2);
+    static_assert((W / 2) * ND * 4 * 64 * 16 <= sizeof(sK) &&
+                  (W / 2) * 2 * 64 * 4 <= sizeof(sV), "merge staging fits the stages");
+    if (late) {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig)
+          sO[(pw * ND * 4 + dt * 4 + ig) * 64 + lane] =
+              f32x4{oacc[0][dt][4 * ig], oacc[0][dt][4 * ig + 1], oacc[0][dt][4 * ig + 2],
+                    oacc[0][dt][4 * ig + 3]};
+      sM[(pw * 2) * 64 + lane] = m_run[0];
+      sM[(pw * 2 + 1) * 64 + lane] = l_run[0];
+    }
+    __syncthreads();
+    if (!late) {
+      const float m2 = sM[(pw * 2) * 64 + lane], l2 = sM[(pw * 2 + 1) * 64 + lane];
+      const float m = fmaxf(m_run[0], m2);
+      const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m);
+      const float a2 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const f32x4 o2 = sO[(pw * ND * 4 + dt * 4 + ig) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            oacc[0][dt][4 * ig + e] = fmaf(oacc[0][dt][4 * ig + e], a1, o2[e] * a2);
+        }
+      l_run[0] = fmaf(l_run[0], a1, l2 * a2);
+      m_run[0] = m;
+    }
+  }
+  const bool writes = !(split && late);
 
   // epilogue
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (!qvalid[nt]) continue;
+    if (!writes || !qvalid[nt]) continue;
     const size_t orow = (static_cast<size_t>(bh) * n_q + qrow_id[nt]) * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
@@ -905,26 +988,33 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
   if (lse != nullptr) lse[static_cast<size_t>(bh) * n_q + qrow_id] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+template <int D, bool OF, bool PERM, bool SPLIT>
+hipError_t launch_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items,
+                       const WorkItem *lists, int32_t *ctl, int grid, hipStream_t s) {
+  constexpr int kW = attn_waves<D>();
+  hipLaunchKernelGGL((attn_bf16_kernel<D, OF, PERM, kW, SPLIT>), dim3(grid), dim3(64 * kW), 0, s,
+                     static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+                     static_cast<const uint16_t *>(a.v), a.o, a.lse, PERM ? a.q_perm : nullptr,
+                     PERM ? a.k_perm : nullptr, a.q_off, a.k_off, a.kept_count, a.kept_idx,
+                     a.kept_stride, work, cap, n_items, lists, ctl, a.n_q, a.n_k, a.nqb, a.nkb,
+                     a.dense, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+// the split-mode instantiation serves Q blocks of at most half a tile on average
+inline bool attn_split_mode(const AttnArgs &a) {
+  return !a.dense && a.nqb > 0 && static_cast<long long>(a.nqb) * (kQTile / 2) >= a.n_q;
+}
+
 template <int D, bool OF>
 hipError_t run_bf16(const AttnArgs &a, const WorkItem *work, int cap, int n_items,
                     const WorkItem *lists, int32_t *ctl, int grid, hipStream_t s) {
-  constexpr int kW = attn_waves<D>();
-  if (a.q_perm != nullptr) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, OF, true, kW>), dim3(grid), dim3(64 * kW), 0, s,
-                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                       static_cast<const uint16_t *>(a.v), a.o, a.lse, a.q_perm, a.k_perm,
-                       a.q_off, a.k_off, a.kept_count, a.kept_idx, a.kept_stride, work, cap,
-                       n_items, lists, ctl, a.n_q, a.n_k, a.nqb, a.nkb, a.dense,
-                       a.scale * kLog2e);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, OF, false, kW>), dim3(grid), dim3(64 * kW), 0, s,
-                     static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                     static_cast<const uint16_t *>(a.v), a.o, a.lse, nullptr, nullptr, a.q_off,
-                     a.k_off,
-                     a.kept_count, a.kept_idx, a.kept_stride, work, cap, n_items, lists, ctl,
-                     a.n_q, a.n_k, a.nqb, a.nkb, a.dense, a.scale * kLog2e);
-  return hipGetLastError();
+  const bool perm = a.q_perm != nullptr;
+  if (attn_split_mode(a))
+    return perm ? launch_bf16<D, OF, true, true>(a, work, cap, n_items, lists, ctl, grid, s)
+                : launch_bf16<D, OF, false, true>(a, work, cap, n_items, lists, ctl, grid, s);
+  return perm ? launch_bf16<D, OF, true, false>(a, work, cap, n_items, lists, ctl, grid, s)
+              : launch_bf16<D, OF, false, false>(a, work, cap, n_items, lists, ctl, grid, s);
 }
 
 template <int D, bool OF>
@@ -1015,7 +1105,7 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
                        qcost);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(a.bh), dim3(kThreads), 0, s, a.q_off, qcost,
-                       a.nqb, cap, w, hinfo);
+                       a.nqb, cap, a.dtype == SVA_BF16 && attn_split_mode(a) ? 1 : 0, w, hinfo);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.dtype == SVA_BF16) {
       hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, w, hinfo, a.bh,

@@ -194,6 +194,50 @@ def test_one_key_blocks_and_empty_blocks(bf16):
     check_lse(host(lse)[0, 0], rl, 1e-3 if bf16 else 1e-5)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_pairs_on_small_query_blocks(d):
+    # Q blocks of at most 128 rows (so the two waves of a SIMD split each
+    # chunk's keys): key lists of 5, 20 and 32 keys leave the second key half
+    # empty in every chunk, others end a chunk with 1..32 keys; one query
+    # block keeps nothing, one holds a single row
+    rng = np.random.default_rng(33 + d)
+    heads, nq = 2, 700
+    qsizes = np.array([128, 1, 100, 128, 64, 33, 120, 126], np.int32)
+    assert qsizes.sum() == nq
+    ksizes = np.array([5, 20, 32, 1, 64, 97, 128, 3, 40, 250, 7, 33], np.int32)
+    nk, nqb, nkb = int(ksizes.sum()), qsizes.size, ksizes.size
+    qoff = np.tile(np.concatenate([[0], np.cumsum(qsizes)]).astype(np.int32), (1, heads, 1))
+    koff = np.tile(np.concatenate([[0], np.cumsum(ksizes)]).astype(np.int32), (1, heads, 1))
+    masks = rng.random((1, heads, nqb, nkb)) < 0.3
+    masks[0, :, 0] = False
+    masks[0, :, 0, 0] = True            # 5 keys
+    masks[0, :, 1] = False
+    masks[0, :, 1, 1] = True            # 20 keys, a 1-row query block
+    masks[0, :, 2] = False
+    masks[0, :, 2, [2, 3]] = True       # 33 keys
+    masks[0, 0, 3] = False              # keeps nothing (head 0)
+    cnt, idx = synth.mask_to_ell(masks)
+    q = rand_inputs((1, heads, nq, d), 80, "bf16")
+    k = rand_inputs((1, heads, nk, d), 81, "bf16")
+    v = rand_inputs((1, heads, nk, d), 82, "bf16")
+    scale = 1 / math.sqrt(d)
+    T = torch.bfloat16
+    o, lse = sva_block_sparse_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T),
+                                   to_dev(qoff, torch.int32), to_dev(koff, torch.int32),
+                                   to_dev(cnt, torch.int32), to_dev(idx, torch.int32), scale,
+                                   want_lse=True)
+    o, lse = host(o), host(lse)
+    for h in range(heads):
+        aq = np.repeat(np.arange(nqb), qsizes)
+        ak = np.repeat(np.arange(nkb), ksizes)
+        ro, rl = oracle.cluster_sparse_attention(q[0, h], k[0, h], v[0, h], aq, ak, masks[0, h],
+                                                 np.float32(scale))
+        check_attention(o[0, h], ro, True, f"head {h}")
+        check_lse(lse[0, h], rl, 1e-3)
+    rows3 = slice(int(qoff[0, 0, 3]), int(qoff[0, 0, 4]))
+    assert (o[0, 0, rows3] == 0).all() and np.isneginf(lse[0, 0, rows3]).all()
+
+
 def test_kept_list_longer_than_one_lds_segment():
     # 1300 two-key blocks, all kept: the kept list is walked in several segments
     rng = np.random.default_rng(5)
