@@ -532,8 +532,8 @@ def bench_adaptive(args) -> int:
     calib_s = time.perf_counter() - t0
     layer = AdaptiveSparseVideoAttention(cfg.heads, cfg.n, cfg.d, cq, ck, cfg.iters, cfg.top_p,
                                          device=dev)
-    inits = [(strided_rows(t["q"][:, h0:h1], g.cq), strided_rows(t["k"][:, h0:h1], g.ck))
-             for h0, h1, g in layer.groups]
+    inits = [(strided_rows(t["q"][:, hs], g.cq), strided_rows(t["k"][:, hs], g.ck))
+             for hs, g in layer.groups]
     iq, ik = [a for a, _ in inits], [b for _, b in inits]
     stages = ("layer",)
 

@@ -315,6 +315,23 @@ int32_t sva_unpermute(const void *o_perm, const int32_t *perm, int32_t dtype, in
                       int32_t heads, int32_t n, int32_t d, void *o, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * sva_gather_slices -- moves whole (b, h) slices between a tensor and a packed
+ * one, so that heads that share their cluster counts (one C_q and C_k per
+ * head: the density follows the content, Sparse VideoGen2, section 2.b) run as
+ * one group of consecutive slices:
+ *   scatter = 0:  dst slice i = src slice idx[i]  (gather into the pack)
+ *   scatter = 1:  dst slice idx[i] = src slice i  (scatter back)
+ *   src, dst     device memory, 16-byte aligned, must not overlap
+ *   idx          [n_idx] int32 DEVICE array of slice indices; the caller
+ *                guarantees they lie in the tensor and (scatter) are distinct
+ *   slice_bytes  bytes per slice, a positive multiple of 16
+ * Returns SVA_EINVAL for a bad argument, SVA_EHIP if the launch fails;
+ * asynchronous on stream.
+ * ------------------------------------------------------------------------ */
+int32_t sva_gather_slices(const void *src, void *dst, const int32_t *idx, int32_t n_idx,
+                          int64_t slice_bytes, int32_t scatter, void *stream);
+
+/* ---------------------------------------------------------------------------
  * sva_full_attn -- dense softmax attention over all keys (density 1.0), the
  * baseline the sparse layer is measured against.  Same kernels and the same
  * numerics as sva_block_sparse_attn with a single block holding every key.

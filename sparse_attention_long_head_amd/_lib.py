@@ -50,6 +50,7 @@ SIGNATURES = {
     "sva_block_sparse_attn_perm": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P,
                                         _I, _P, _P, _I, _F, _P, _I, _P, _P, _Z, _P]),
     "sva_unpermute": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "sva_gather_slices": (_I, [_P, _P, _P, _I, ctypes.c_int64, _I, _P]),
     "sva_full_attn_workspace_bytes": (_Z, [_I, _I, _I]),
     "sva_full_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _Z, _P]),
     "sva_check_mfma_rounding": (_I, [_P, _P]),
@@ -343,6 +344,23 @@ def sva_unpermute(o_perm: torch.Tensor, perm: torch.Tensor, o: Optional[torch.Te
     _check(lib().sva_unpermute(_ptr(o_perm), _ptr(perm), _dtype_code(o_perm), b, h, n, d, _ptr(o),
                                _stream(o_perm)), "sva_unpermute")
     return o
+
+
+def sva_gather_slices(src: torch.Tensor, idx: torch.Tensor, dst: torch.Tensor,
+                      scatter: bool = False):
+    """Whole leading-dimension slices: dst[i] = src[idx[i]] (gather), or
+    dst[idx[i]] = src[i] (scatter).  src and dst are contiguous with equal
+    slice shapes; idx is an int32 device tensor."""
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("tensors passed to libsva must be contiguous")
+    if src.shape[1:] != dst.shape[1:] or src.dtype != dst.dtype:
+        raise ValueError("src and dst slices must have one shape and dtype")
+    if idx.dtype != torch.int32 or idx.device != src.device:
+        raise ValueError("idx must be an int32 tensor on the tensors' device")
+    slice_bytes = src[0].numel() * src.element_size()
+    _check(lib().sva_gather_slices(_ptr(src), _ptr(dst), _ptr(idx), idx.numel(), slice_bytes,
+                                   1 if scatter else 0, _stream(src)), "sva_gather_slices")
+    return dst
 
 
 def sva_full_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,

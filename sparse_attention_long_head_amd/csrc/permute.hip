@@ -167,6 +167,21 @@ __global__ __launch_bounds__(kThreads) void move_rows_kernel(const u32x4 *__rest
   else dst[(self << lcpr) + part] = src[(other << lcpr) + part];
 }
 
+// whole slices of 16-byte pieces: packed slice i <-> slice idx[i]; one
+// grid row per packed slice, grid-stride over its pieces
+__global__ __launch_bounds__(kThreads) void move_slices_kernel(const u32x4 *__restrict__ src,
+                                                               u32x4 *__restrict__ dst,
+                                                               const int32_t *__restrict__ idx,
+                                                               long long pieces, int scatter) {
+  const long long i = blockIdx.y;
+  const long long other = idx[i];
+  const u32x4 *s = src + (scatter ? i : other) * pieces;
+  u32x4 *d = dst + (scatter ? other : i) * pieces;
+  for (long long p = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x; p < pieces;
+       p += static_cast<long long>(gridDim.x) * kThreads)
+    d[p] = s[p];
+}
+
 __global__ void fill_i32_kernel(int32_t *p, int32_t value, size_t count) {
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -222,6 +237,18 @@ hipError_t launch_gather_rows(const void *src, void *dst, const int32_t *perm, i
   hipLaunchKernelGGL(move_rows_kernel, dim3((n + rows_per_blk - 1) / rows_per_blk, bh),
                      dim3(kThreads), 0, s, static_cast<const u32x4 *>(src),
                      static_cast<u32x4 *>(dst), perm, n, lcpr, scatter);
+  return hipGetLastError();
+}
+
+hipError_t launch_move_slices(const void *src, void *dst, const int32_t *idx, int32_t n_idx,
+                              long long slice_bytes, int32_t scatter, hipStream_t s) {
+  if (n_idx == 0) return hipSuccess;
+  const long long pieces = slice_bytes / 16;
+  const long long want = (pieces + kThreads - 1) / kThreads;
+  const int gx = static_cast<int>(want < 512 ? want : 512);
+  hipLaunchKernelGGL(move_slices_kernel, dim3(gx, n_idx), dim3(kThreads), 0, s,
+                     static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), idx, pieces,
+                     scatter);
   return hipGetLastError();
 }
 

@@ -146,6 +146,22 @@ int32_t sva_permute(const int32_t *assign, int32_t c, int32_t batch, int32_t hea
   return hip_status(e, fn);
 }
 
+int32_t sva_gather_slices(const void *src, void *dst, const int32_t *idx, int32_t n_idx,
+                          int64_t slice_bytes, int32_t scatter, void *stream) {
+  const char *fn = "sva_gather_slices";
+  if (!src || !dst || !idx) return fail(SVA_EINVAL, "%s: src, dst and idx must be non-NULL", fn);
+  if (n_idx < 0 || n_idx > 65535)
+    return fail(SVA_EINVAL, "%s: need 0 <= n_idx <= 65535 (n_idx=%d)", fn, n_idx);
+  if (slice_bytes <= 0 || slice_bytes % 16 != 0)
+    return fail(SVA_EINVAL, "%s: slice_bytes must be a positive multiple of 16", fn);
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return fail(SVA_EINVAL, "%s: src and dst must be 16-byte aligned", fn);
+  if (scatter != 0 && scatter != 1) return fail(SVA_EINVAL, "%s: scatter must be 0 or 1", fn);
+  return hip_status(sva::launch_move_slices(src, dst, idx, n_idx, slice_bytes, scatter,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 // ---------------------------------------------------------------------------
 size_t sva_select_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
 

@@ -125,6 +125,8 @@ hipError_t launch_block_means(const void *x, int32_t dtype, int32_t bh, int32_t 
                               int32_t block, float *means, int32_t *sizes, hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t s);
+hipError_t launch_move_slices(const void *src, void *dst, const int32_t *idx, int32_t n_idx,
+                              long long slice_bytes, int32_t scatter, hipStream_t s);
 
 // compute units of the current device (persistent grids); 256 if the query fails
 int device_cus();

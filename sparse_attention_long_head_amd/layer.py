@@ -306,10 +306,12 @@ def choose_clusters(x: torch.Tensor, ladder, iters: int, delta: float = 0.1):
 
 
 class AdaptiveSparseVideoAttention:
-    """The SVG2 layer with its own (C_q, C_k) per head: consecutive heads with
-    equal counts form a group that runs as one ``SparseVideoAttention`` on its
-    head range, writing straight into that range of one output tensor.  Batch 1
-    (a head range of a [1, H, n, d] tensor is contiguous)."""
+    """The SVG2 layer with its own (C_q, C_k) per head.  Heads with equal counts
+    form one group, wherever they sit, that runs as one ``SparseVideoAttention``:
+    a group of consecutive heads works on views of its head range and writes
+    straight into that range of the output; any other group's heads are packed
+    into buffers of their own (sva_gather_slices) and its output scattered back.
+    Batch 1 (a head of a [1, H, n, d] tensor is one contiguous slice)."""
 
     def __init__(self, heads: int, n: int, d: int, cq_per_head, ck_per_head, iters: int,
                  top_p: float, dtype: torch.dtype = torch.bfloat16, device="cuda", **kw):
@@ -318,28 +320,46 @@ class AdaptiveSparseVideoAttention:
             raise ValueError("one C_q and one C_k per head")
         dev = torch.device(device)
         self.o = torch.empty((1, heads, n, d), dtype=dtype, device=dev)
-        self.groups = []          # (h0, h1, layer)
-        h0 = 0
-        while h0 < heads:
-            h1 = h0 + 1
-            while h1 < heads and (cq_per_head[h1], ck_per_head[h1]) == (cq_per_head[h0],
-                                                                      ck_per_head[h0]):
-                h1 += 1
-            layer = SparseVideoAttention(1, h1 - h0, n, d, cq_per_head[h0], ck_per_head[h0],
-                                         iters, top_p, dtype=dtype, device=dev,
-                                         out=self.o[:, h0:h1], **kw)
-            self.groups.append((h0, h1, layer))
-            h0 = h1
+        order = {}
+        for h, key in enumerate(zip(cq_per_head, ck_per_head)):
+            order.setdefault(key, []).append(h)
+        self.groups = []          # (heads, layer)
+        self._packs = []          # None for a head range, else (idx, q, k, v, o) buffers
+        for (cq, ck), hs in order.items():
+            g = len(hs)
+            if hs == list(range(hs[0], hs[0] + g)):
+                layer = SparseVideoAttention(1, g, n, d, cq, ck, iters, top_p, dtype=dtype,
+                                             device=dev, out=self.o[:, hs[0]:hs[0] + g], **kw)
+                pack = None
+            else:
+                po = torch.empty((1, g, n, d), dtype=dtype, device=dev)
+                layer = SparseVideoAttention(1, g, n, d, cq, ck, iters, top_p, dtype=dtype,
+                                             device=dev, out=po, **kw)
+                idx = torch.tensor(hs, dtype=torch.int32, device=dev)
+                pack = (idx, *(torch.empty((1, g, n, d), dtype=dtype, device=dev)
+                               for _ in range(3)), po)
+            self.groups.append((hs, layer))
+            self._packs.append(pack)
 
     def forward(self, q, k, v, init_q=None, init_k=None) -> torch.Tensor:
-        """init_q / init_k: one initial-centroid tensor per group ([1, g, C, d]),
-        or None for a warm start from the previous call."""
-        for gi, (h0, h1, layer) in enumerate(self.groups):
-            layer(q[:, h0:h1], k[:, h0:h1], v[:, h0:h1],
-                  None if init_q is None else init_q[gi], None if init_k is None else init_k[gi])
+        """init_q / init_k: one initial-centroid tensor per group ([1, g, C, d],
+        the group's heads in ascending order), or None for a warm start from the
+        previous call."""
+        for gi, ((hs, layer), pack) in enumerate(zip(self.groups, self._packs)):
+            iq = None if init_q is None else init_q[gi]
+            ik = None if init_k is None else init_k[gi]
+            if pack is None:
+                h0, h1 = hs[0], hs[0] + len(hs)
+                layer(q[:, h0:h1], k[:, h0:h1], v[:, h0:h1], iq, ik)
+            else:
+                idx, pq, pk, pv, po = pack
+                for src, dst in ((q, pq), (k, pk), (v, pv)):
+                    L.sva_gather_slices(src[0], idx, dst[0])
+                layer(pq, pk, pv, iq, ik)
+                L.sva_gather_slices(po[0], idx, self.o[0], scatter=True)
         return self.o
 
     __call__ = forward
 
     def kept_pairs(self) -> int:
-        return sum(layer.kept_pairs() for _, _, layer in self.groups)
+        return sum(layer.kept_pairs() for _, layer in self.groups)

@@ -198,3 +198,15 @@ def test_noalloc_attention_rejects_a_schedule_beyond_its_scratch(L):
     assert "static scratch" in L.last_error()
     assert lib.sva_block_sparse_attn_noalloc(P, P, P, 1, 1, 2, 1000, 1000, 128, P, 8, P, 0, P, P,
                                              8, 0.088, P, 1, None, None) == L.SVA_EINVAL
+
+
+def test_gather_slices_validation(L):
+    lib = L.lib()
+    assert lib.sva_gather_slices(None, P, P, 2, 4096, 0, None) == L.SVA_EINVAL
+    assert lib.sva_gather_slices(P, P, None, 2, 4096, 0, None) == L.SVA_EINVAL
+    assert lib.sva_gather_slices(P, P, P, -1, 4096, 0, None) == L.SVA_EINVAL
+    assert lib.sva_gather_slices(P, P, P, 2, 4100, 0, None) == L.SVA_EINVAL   # not 16-byte pieces
+    assert lib.sva_gather_slices(P, P, P, 2, 0, 0, None) == L.SVA_EINVAL
+    assert lib.sva_gather_slices(ctypes.c_void_p(264), P, P, 2, 4096, 0, None) == L.SVA_EINVAL
+    assert lib.sva_gather_slices(P, P, P, 2, 4096, 2, None) == L.SVA_EINVAL
+    assert L.last_error().startswith("sva_gather_slices")

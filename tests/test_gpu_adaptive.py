@@ -3,10 +3,12 @@
 * sva_cluster_spread against the same sums in fp64 NumPy (J: the k-means
   objective under the GPU's assignment and centroids; T: the scatter about the
   mean);
-* a layer whose heads have different (C_q, C_k), head by head against the fp64
-  oracle: the last k-means iteration in lockstep, the top-p selection in
-  lockstep, and the output against the oracle's attention under the GPU's own
-  clusters and mask; each head group equals a plain layer run on its heads;
+* a layer whose heads have different (C_q, C_k), two of them equal but not
+  adjacent (a packed group), head by head against the fp64 oracle: the last
+  k-means iteration in lockstep, the top-p selection in lockstep, and the
+  output against the oracle's attention under the GPU's own clusters and mask;
+  each head group equals a plain layer run on its heads; the slice gather and
+  scatter against torch indexing;
 * the rule (smallest C of a ladder within (1 + delta) of the objective at the
   largest C) on heads drawn with few and with many mixture regions.
 """
@@ -18,7 +20,8 @@ import oracle
 import synth
 from parity import assign_parity, check_attention, device, host, to_dev
 from sparse_attention_long_head_amd import (AdaptiveSparseVideoAttention, SparseVideoAttention,
-                                            choose_clusters, sva_cluster_spread, sva_kmeans)
+                                            choose_clusters, sva_cluster_spread,
+                                            sva_gather_slices, sva_kmeans)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,8 +48,8 @@ def test_cluster_spread_parity(dtype, d):
     assert np.array_equal(sp, host(sva_cluster_spread(xt, c, cent, a)))
 
 
-CQ = [30, 30, 60, 20]
-CK = [150, 150, 300, 90]
+CQ = [30, 60, 30, 20]
+CK = [150, 300, 150, 90]
 
 
 @pytest.fixture(scope="module")
@@ -57,14 +60,14 @@ def adaptive():
     t = {n: to_dev(x[n], torch.bfloat16) for n in "qkv"}
     layer = AdaptiveSparseVideoAttention(cfg.heads, cfg.n, cfg.d, CQ, CK, cfg.iters, cfg.top_p,
                                          device=dev)
-    assert [(h0, h1) for h0, h1, _ in layer.groups] == [(0, 2), (2, 3), (3, 4)]
+    # heads 0 and 2 share their counts (a packed group), heads 1 and 3 are alone
+    assert [hs for hs, _ in layer.groups] == [[0, 2], [1], [3]]
     inits_q, inits_k = [], []
-    for h0, h1, g in layer.groups:
-        hs = tuple(range(h0, h1))
+    for hs, g in layer.groups:
         inits_q.append(to_dev(synth.gather_init(
-            x["q"][:, h0:h1], synth.kmeans_init_indices(cfg, "q", g.cq, heads=hs))))
+            x["q"][:, hs], synth.kmeans_init_indices(cfg, "q", g.cq, heads=tuple(hs)))))
         inits_k.append(to_dev(synth.gather_init(
-            x["k"][:, h0:h1], synth.kmeans_init_indices(cfg, "k", g.ck, heads=hs))))
+            x["k"][:, hs], synth.kmeans_init_indices(cfg, "k", g.ck, heads=tuple(hs)))))
     o = layer(t["q"], t["k"], t["v"], inits_q, inits_k)
     torch.cuda.synchronize()
     return cfg, x, t, layer, inits_q, inits_k, host(o)
@@ -73,18 +76,16 @@ def adaptive():
 def test_heads_with_different_c_match_the_oracle(adaptive):
     cfg, x, t, layer, inits_q, inits_k, o = adaptive
     ties = 0
-    for gi, (h0, h1, g) in enumerate(layer.groups):
+    for gi, (hs, g) in enumerate(layer.groups):
         for name, init, c, assign in (("q", inits_q[gi], g.cq, g.assign_q),
                                       ("k", inits_k[gi], g.ck, g.assign_k)):
             cent = init.clone()
-            sva_kmeans(t[name][:, h0:h1], c, cfg.iters - 1, cent)     # entering the last step
+            sva_kmeans(t[name][:, hs].contiguous(), c, cfg.iters - 1, cent)   # entering the last step
             before = host(cent).astype(np.float64)
-            for j in range(h1 - h0):
-                ref, margin = oracle.assign_step(x[name][0, h0 + j].astype(np.float64),
-                                                 before[0, j])
-                ties += assign_parity(host(assign)[0, j], ref, margin, f"{name} head {h0 + j}")
-        for j in range(h1 - h0):
-            h = h0 + j
+            for j, h in enumerate(hs):
+                ref, margin = oracle.assign_step(x[name][0, h].astype(np.float64), before[0, j])
+                ties += assign_parity(host(assign)[0, j], ref, margin, f"{name} head {h}")
+        for j, h in enumerate(hs):
             r = oracle.top_p_select(oracle.centroid_scores(host(g.cent_q)[0, j],
                                                            host(g.cent_k)[0, j], g.scale),
                                     host(g.sizes_q)[0, j], host(g.sizes_k)[0, j], cfg.top_p)
@@ -101,12 +102,26 @@ def test_heads_with_different_c_match_the_oracle(adaptive):
 
 def test_each_group_equals_a_plain_layer(adaptive):
     cfg, x, t, layer, inits_q, inits_k, o = adaptive
-    for gi, (h0, h1, g) in enumerate(layer.groups):
-        plain = SparseVideoAttention(1, h1 - h0, cfg.n, cfg.d, g.cq, g.ck, cfg.iters, cfg.top_p,
+    for gi, (hs, g) in enumerate(layer.groups):
+        plain = SparseVideoAttention(1, len(hs), cfg.n, cfg.d, g.cq, g.ck, cfg.iters, cfg.top_p,
                                      device=device())
-        op = plain(t["q"][:, h0:h1].contiguous(), t["k"][:, h0:h1].contiguous(),
-                   t["v"][:, h0:h1].contiguous(), inits_q[gi], inits_k[gi])
-        assert np.array_equal(host(op), o[:, h0:h1])
+        op = plain(t["q"][:, hs].contiguous(), t["k"][:, hs].contiguous(),
+                   t["v"][:, hs].contiguous(), inits_q[gi], inits_k[gi])
+        assert np.array_equal(host(op), o[:, hs])
+
+
+def test_gather_slices_round_trip():
+    dev = device()
+    src = torch.randn(7, 33, 64, device=dev).to(torch.bfloat16)
+    idx = torch.tensor([5, 0, 3], dtype=torch.int32, device=dev)
+    packed = torch.empty(3, 33, 64, dtype=torch.bfloat16, device=dev)
+    sva_gather_slices(src, idx, packed)
+    assert torch.equal(packed, src[idx.long()])
+    back = torch.zeros_like(src)
+    sva_gather_slices(packed, idx, back, scatter=True)
+    ref = torch.zeros_like(src)
+    ref[idx.long()] = src[idx.long()]
+    assert torch.equal(back, ref)
 
 
 def test_rule_gives_fewer_clusters_to_simpler_content():
