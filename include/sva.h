@@ -37,8 +37,8 @@
  *   SVA_EWORKSPACE and launches nothing; a HIP launch failure returns
  *   SVA_EHIP.  sva_last_error() then gives a message (thread-local; valid
  *   until the next call on the same thread).  Device-side preconditions
- *   (monotone offsets, in-range indices) are documented per call and are not
- *   checked on the device.
+ *   (monotone offsets, in-range indices) are documented per call; they are
+ *   checked on the device only in the debug mode of sva_set_debug_checks.
  * - Results are deterministic: identical inputs give bitwise-identical
  *   outputs.  Calls on different streams may overlap if their buffers differ.
  */
@@ -67,6 +67,23 @@ const char *sva_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t sva_abi_version(void);
+
+/* Debug mode (process-wide, off by default).  While on, every block-sparse
+ * attention call (sva_block_sparse_attn, _perm, _noalloc) first runs a check
+ * kernel on its stream over the device arrays the call reads, waits for it,
+ * and returns SVA_EINVAL without launching the attention if any of these
+ * preconditions of the block layout (Sparse VideoGen2, section 2.c: the
+ * kernel over blocks of varying size) fails:
+ *   q_offsets / k_offsets of each slice monotone, from >= 0 to <= n_q / n_k;
+ *   kept_count in [0, min(kept_stride, n_kblocks)];
+ *   each listed kept_idx in [0, n_kblocks) (at most kept_stride read per row);
+ *   q_perm / k_perm entries in [0, n_q) / [0, n_k).
+ * The message names the violated ones.  The check synchronises the stream, so
+ * debug mode is for testing, not for graph capture or timed runs.  It uses a
+ * static device word per GPU (no allocation); overlapping checked calls on
+ * one GPU may report each other's violations.  on = 0 turns it off.
+ * Returns SVA_OK. */
+int32_t sva_set_debug_checks(int32_t on);
 
 /* ---------------------------------------------------------------------------
  * sva_kmeans -- Lloyd k-means of every (b,h) slice of x, independently.

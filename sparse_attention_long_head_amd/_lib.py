@@ -30,6 +30,7 @@ _F = ctypes.c_float
 SIGNATURES = {
     "sva_last_error": (ctypes.c_char_p, []),
     "sva_abi_version": (_I, []),
+    "sva_set_debug_checks": (_I, [_I]),
     "sva_kmeans_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "sva_kmeans": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "sva_cluster_spread": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
@@ -77,6 +78,12 @@ def lib() -> ctypes.CDLL:
 
 def last_error() -> str:
     return lib().sva_last_error().decode()
+
+
+def sva_set_debug_checks(on: bool) -> None:
+    """Turn the device-side precondition checks of the block-sparse calls on
+    or off (process-wide; each checked call waits for its check kernel)."""
+    _check(lib().sva_set_debug_checks(1 if on else 0), "sva_set_debug_checks")
 
 
 def _check(status: int, name: str) -> None:

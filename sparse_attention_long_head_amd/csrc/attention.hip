@@ -219,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void attn_cost_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+  L = max(L, 0);   // offsets that break monotonicity never give a negative cost
   if (lane == 0) qcost[e] = (L + kKT - 1) / kKT + kItemFixed;
 }
 
@@ -879,8 +880,10 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
   // epilogue
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    // l_tot is 0 exactly when the row saw no key (O = 0, LSE = -inf); a NaN
+    // that reached the row's sum takes the other branch and stays NaN
     const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot != 0.f ? 1.f / l_tot : 0.f;
     if (!writes || !qvalid[nt]) continue;
     const size_t orow = (static_cast<size_t>(bh) * n_q + qrow_id[nt]) * D;
 #pragma unroll
@@ -899,7 +902,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       }
     if (h == 0 && lse != nullptr)
       lse[static_cast<size_t>(bh) * n_q + qrow_id[nt]] =
-          l_tot > 0.f ? (m_run[nt] + __log2f(l_tot)) * kLn2 : -INFINITY;
+          l_tot != 0.f ? (m_run[nt] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
   };
 
@@ -978,14 +981,14 @@ __global__ __launch_bounds__(kQTile) void attn_f32_kernel(
     }
   }
   if (!qvalid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l != 0.f ? 1.f / l : 0.f;   // l = 0: no key; NaN stays NaN
   const size_t orow = (static_cast<size_t>(bh) * n_q + qrow_id) * D;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     if constexpr (OUT_F32) static_cast<float *>(o)[orow + i] = acc[i] * inv;
     else static_cast<uint16_t *>(o)[orow + i] = f32_to_bf16_bits(acc[i] * inv);
   }
-  if (lse != nullptr) lse[static_cast<size_t>(bh) * n_q + qrow_id] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (lse != nullptr) lse[static_cast<size_t>(bh) * n_q + qrow_id] = l != 0.f ? m + logf(l) : -INFINITY;
 }
 
 template <int D, bool OF, bool PERM, bool SPLIT>
@@ -1080,6 +1083,85 @@ void *attn_static_scratch(hipError_t *err) {
   }
   *err = hipSuccess;
   return ptr[dev];
+}
+
+// ---------------------------------------------------------------------------
+// Debug checks of the device preconditions of the block-sparse calls (set by
+// sva_set_debug_checks): one thread per (slice, Q block) checks that block's
+// Q offsets, kept count and kept K block ids, one per (slice, K block) that
+// block's K offsets, and grid-stride threads the permutations.  Violations set
+// bits of a flag kept in a static device word per GPU (looked up like the
+// static scratch); the caller clears it first and reads it back after.
+// ---------------------------------------------------------------------------
+static __device__ int32_t debug_flag_word[4];
+
+__global__ __launch_bounds__(kThreads) void attn_index_check_kernel(AttnArgs a, int32_t *flag) {
+  const int bh = blockIdx.y;
+  const long long t = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  int bits = 0;
+  if (t < a.nqb) {
+    const int qb = static_cast<int>(t);
+    const int32_t *qo = a.q_off + static_cast<size_t>(bh) * (a.nqb + 1);
+    if (qo[qb] < 0 || qo[qb] > qo[qb + 1] || qo[qb + 1] > a.n_q) bits |= kDebugQOffsets;
+    const size_t e = static_cast<size_t>(bh) * a.nqb + qb;
+    const int cnt = a.kept_count[e];
+    if (cnt < 0 || cnt > a.kept_stride || cnt > a.nkb) bits |= kDebugKeptCount;
+    const int m = min(max(cnt, 0), a.kept_stride);
+    for (int j = 0; j < m; ++j) {
+      const int b = a.kept_idx[e * a.kept_stride + j];
+      if (b < 0 || b >= a.nkb) bits |= kDebugKeptIdx;
+    }
+  }
+  if (t < a.nkb) {
+    const int kb = static_cast<int>(t);
+    const int32_t *ko = a.k_off + static_cast<size_t>(bh) * (a.nkb + 1);
+    if (ko[kb] < 0 || ko[kb] > ko[kb + 1] || ko[kb + 1] > a.n_k) bits |= kDebugKOffsets;
+  }
+  const long long stride = static_cast<long long>(gridDim.x) * kThreads;
+  if (a.q_perm != nullptr)
+    for (long long i = t; i < a.n_q; i += stride) {
+      const int r = a.q_perm[static_cast<size_t>(bh) * a.n_q + i];
+      if (r < 0 || r >= a.n_q) bits |= kDebugQPerm;
+    }
+  if (a.k_perm != nullptr)
+    for (long long i = t; i < a.n_k; i += stride) {
+      const int r = a.k_perm[static_cast<size_t>(bh) * a.n_k + i];
+      if (r < 0 || r >= a.n_k) bits |= kDebugKPerm;
+    }
+  if (bits) atomicOr(flag, bits);
+}
+
+__global__ void debug_flag_clear_kernel(int32_t *flag) { flag[0] = 0; }
+
+hipError_t attn_debug_check(const AttnArgs &a, hipStream_t s, int32_t *bits) {
+  static std::mutex mu;
+  static int32_t *ptr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int32_t *flag;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+      void *p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(debug_flag_word));
+      if (e != hipSuccess) return e;
+      ptr[dev] = static_cast<int32_t *>(p);
+    }
+    flag = ptr[dev];
+  }
+  hipLaunchKernelGGL(debug_flag_clear_kernel, dim3(1), dim3(1), 0, s, flag);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int most = std::max(std::max(a.nqb, a.nkb), 1);
+  const int gx = std::min((most + kThreads - 1) / kThreads, 1024);
+  hipLaunchKernelGGL(attn_index_check_kernel, dim3(gx, a.bh), dim3(kThreads), 0, s, a, flag);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int32_t h = 0;
+  if ((e = hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  *bits = h;
+  return hipSuccess;
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {

@@ -1,10 +1,13 @@
 // extern "C" entry points of libsva: host-side validation, workspace carving
-// and kernel dispatch.  Nothing here allocates, frees or synchronises; every
-// check runs before the first launch, so a rejected call launches nothing.
+// and kernel dispatch.  Nothing here allocates, frees or synchronises (except
+// the opt-in debug checks of device preconditions, which wait for their
+// check kernel); every host check runs before the first launch, so a rejected
+// call launches nothing.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/sva.h"
@@ -13,6 +16,7 @@
 namespace {
 
 thread_local std::string g_err;
+std::atomic<bool> g_debug_checks{false};   // sva_set_debug_checks
 
 int32_t fail(int32_t code, const char *fmt, ...) {
   char buf[512];
@@ -312,7 +316,26 @@ static int32_t block_sparse(const char *fn, const void *q, const void *k, const 
   sva::AttnArgs a{q, k, v, o, lse, q_offsets, k_offsets, kept_count, kept_idx, q_perm, k_perm,
                   kept_stride, batch * heads, n_q, n_k, d, n_qblocks, n_kblocks, dtype, o_dtype,
                   0, scale, ws};
+  if (g_debug_checks.load()) {
+    int32_t bits = 0;
+    hipError_t e = sva::attn_debug_check(a, static_cast<hipStream_t>(stream), &bits);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (bits != 0)
+      return fail(SVA_EINVAL,
+                  "%s: debug check: device preconditions violated:%s%s%s%s%s%s", fn,
+                  bits & sva::kDebugQOffsets ? " q_offsets not monotone in [0, n_q]" : "",
+                  bits & sva::kDebugKOffsets ? " k_offsets not monotone in [0, n_k]" : "",
+                  bits & sva::kDebugKeptCount ? " kept_count outside [0, min(kept_stride, n_kblocks)]" : "",
+                  bits & sva::kDebugKeptIdx ? " kept_idx outside [0, n_kblocks)" : "",
+                  bits & sva::kDebugQPerm ? " q_perm outside [0, n_q)" : "",
+                  bits & sva::kDebugKPerm ? " k_perm outside [0, n_k)" : "");
+  }
   return hip_status(sva::launch_attention(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t sva_set_debug_checks(int32_t on) {
+  g_debug_checks.store(on != 0);
+  return SVA_OK;
 }
 
 int32_t sva_block_sparse_attn(const void *q, const void *k, const void *v, int32_t dtype,

@@ -68,6 +68,13 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 // address on the current device (looked up once per device), or NULL with *err
 constexpr size_t kStaticAttnScratch = size_t{8} << 20;
 void *attn_static_scratch(hipError_t *err);
+// debug checks of the block-sparse calls' device preconditions: *bits = the
+// violated ones (0: none); synchronises the stream
+enum : int32_t {
+  kDebugQOffsets = 1, kDebugKOffsets = 2, kDebugKeptCount = 4, kDebugKeptIdx = 8,
+  kDebugQPerm = 16, kDebugKPerm = 32
+};
+hipError_t attn_debug_check(const AttnArgs &a, hipStream_t s, int32_t *bits);
 
 struct KmeansArgs {
   const void *x;

@@ -210,3 +210,23 @@ def test_gather_slices_validation(L):
     assert lib.sva_gather_slices(ctypes.c_void_p(264), P, P, 2, 4096, 0, None) == L.SVA_EINVAL
     assert lib.sva_gather_slices(P, P, P, 2, 4096, 2, None) == L.SVA_EINVAL
     assert L.last_error().startswith("sva_gather_slices")
+
+
+def test_debug_checks_switch(L):
+    """sva_set_debug_checks only sets a flag: host validation still runs first
+    (a bad argument is rejected before any device work), and on a host with no
+    GPU a valid call in debug mode fails in its check with SVA_EHIP."""
+    import torch
+    lib = L.lib()
+    assert lib.sva_set_debug_checks(1) == L.SVA_OK
+    try:
+        ws = lib.sva_attn_workspace_bytes(1, 2, 1000, 8)
+        ok = [P, P, P, 1, 1, 2, 1000, 1000, 128, P, 8, P, 8, P, P, 8, 0.1, P, 1, None, P, ws, None]
+        bad = list(ok)
+        bad[10] = 0
+        assert lib.sva_block_sparse_attn(*bad) == L.SVA_EINVAL
+        if torch.cuda.device_count() == 0:
+            assert lib.sva_block_sparse_attn(*ok) == L.SVA_EHIP
+            assert L.last_error().startswith("sva_block_sparse_attn")
+    finally:
+        assert lib.sva_set_debug_checks(0) == L.SVA_OK

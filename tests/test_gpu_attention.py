@@ -18,7 +18,7 @@ import oracle
 import synth
 from parity import (check_attention, check_lse, device, host, rand_inputs, to_dev)
 from sparse_attention_long_head_amd import (sva_block_sparse_attn, sva_block_sparse_attn_perm,
-                                          sva_full_attn)
+                                          sva_full_attn, sva_set_debug_checks)
 
 pytestmark = pytest.mark.gpu
 
@@ -271,6 +271,103 @@ def test_deterministic():
     a, _ = sva_block_sparse_attn(*args)
     b, _ = sva_block_sparse_attn(*args)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_nan_reaches_exactly_the_rows_that_read_it(bf16):
+    """The NaN rule on the GPU (both kernels; bf16 here also runs the split
+    mode): a NaN in a query row, in a kept K row or in an element of a kept V row
+    puts NaN exactly where the oracle has it (all of O_n and LSE_n, all of O_n
+    and LSE_n, O_n[c] only), and every other output is bitwise the clean run's.
+    A key block that no query block keeps may hold NaN in K and V: nothing
+    reads it."""
+    n, block, heads, d = 1000, 128, 3, 128
+    q, k, v, masks, off, cnt, idx = _uniform_case(n, block, heads, 11, 0.4, bf16, d)
+    masks[1, :, 5] = False                   # head 1: key block 5 kept by nobody
+    cnt, idx = synth.mask_to_ell(masks[None])
+    T = _tdtype(bf16)
+    scale = 1 / math.sqrt(d)
+
+    def run(qq, kk, vv):
+        o, lse = sva_block_sparse_attn(to_dev(qq, T), to_dev(kk, T), to_dev(vv, T),
+                                       to_dev(off, torch.int32), to_dev(off, torch.int32),
+                                       to_dev(cnt, torch.int32), to_dev(idx, torch.int32),
+                                       scale, want_lse=True)
+        return host(o), host(lse)
+
+    o0, l0 = run(q, k, v)
+    qn, kn, vn = q.copy(), k.copy(), v.copy()
+    kn[0, 0, 300, 5] = np.nan                # head 0: one K element (key block 2)
+    vn[0, 1, 450, 7] = np.nan                # head 1: one V element (key block 3)
+    kn[0, 1, 640:768] = np.nan               # head 1: the unkept key block
+    vn[0, 1, 640:768] = np.nan
+    qn[0, 2, 777, 0] = np.nan                # head 2: one query element
+    o, lse = run(qn, kn, vn)
+    for h in range(heads):
+        ro, rl = oracle.block_sparse_attention(qn[0, h], kn[0, h], vn[0, h], masks[h], block,
+                                               np.float32(scale))
+        nan_o, nan_l = np.isnan(ro), np.isnan(rl)
+        assert nan_o.any() and (~nan_o).any(), h
+        assert np.array_equal(np.isnan(o[0, h]), nan_o), h
+        assert np.array_equal(np.isnan(lse[0, h]), nan_l), h
+        assert np.array_equal(o[0, h][~nan_o], o0[0, h][~nan_o]), h
+        assert np.array_equal(lse[0, h][~nan_l], l0[0, h][~nan_l]), h
+
+
+def test_debug_checks_catch_bad_device_indices():
+    """Debug mode: a call whose device arrays break the layout's preconditions
+    is refused with SVA_EINVAL naming the violation, and the attention is not
+    launched; a valid call gives the same bits as without the checks.  Every
+    violation used here would stay inside the buffers even if the attention
+    were launched (ranges of negative length are skipped, ids and rows one past
+    the end land in the next slice)."""
+    n, block, heads, d = 1000, 128, 3, 128
+    q, k, v, masks, off, cnt, idx = _uniform_case(n, block, heads, 5, 0.4, True, d)
+    masks[1, 0, :] = True                    # head 1, block 0 keeps every key block
+    cnt, idx = synth.mask_to_ell(masks[None])
+    nb = masks.shape[-1]
+    qd, kd, vd = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    scale = 1 / math.sqrt(d)
+
+    def call(qoff, koff, c, i, perm=None):
+        if perm is None:
+            return sva_block_sparse_attn(qd, kd, vd, to_dev(qoff, torch.int32),
+                                         to_dev(koff, torch.int32), to_dev(c, torch.int32),
+                                         to_dev(i, torch.int32), scale)[0]
+        return sva_block_sparse_attn_perm(qd, kd, vd, to_dev(perm, torch.int32),
+                                          to_dev(np.tile(np.arange(n), (1, heads, 1)),
+                                                 torch.int32),
+                                          to_dev(qoff, torch.int32), to_dev(koff, torch.int32),
+                                          to_dev(c, torch.int32), to_dev(i, torch.int32),
+                                          scale)[0]
+
+    ref = call(off, off, cnt, idx)
+    sva_set_debug_checks(True)
+    try:
+        assert torch.equal(call(off, off, cnt, idx), ref)
+        bad_q = off.copy()
+        bad_q[0, 0, 2] = 100                 # block 1 = [128, 100): not monotone
+        bad_k = off.copy()
+        bad_k[0, 2, 2] = 320                 # head 2: key block 1 = [128, 320),
+        bad_k[0, 2, 3] = 300                 # block 2 = [320, 300), block 3 = [300, 384)
+        bad_c = cnt.copy()
+        bad_c[0, 1, 0] = nb + 1              # more than the row's stride holds
+        bad_i = idx.copy()
+        bad_i[0, 0, 3, 0] = nb               # a kept id past the last key block
+        bad_p = np.tile(np.arange(n), (1, heads, 1)).astype(np.int32)
+        bad_p[0, 0, 17] = n                  # a query row past the slice
+        for args, perm, what in [((bad_q, off, cnt, idx), None, "q_offsets"),
+                                 ((off, bad_k, cnt, idx), None, "k_offsets"),
+                                 ((off, off, bad_c, idx), None, "kept_count"),
+                                 ((off, off, cnt, bad_i), None, "kept_idx"),
+                                 ((off, off, cnt, idx), bad_p, "q_perm")]:
+            with pytest.raises(RuntimeError, match=what):
+                call(*args, perm=perm)
+        with pytest.raises(RuntimeError, match="q_offsets.*kept_idx"):
+            call(bad_q, off, cnt, bad_i)
+        assert torch.equal(call(off, off, cnt, idx), ref)   # nothing sticks
+    finally:
+        sva_set_debug_checks(False)
 
 
 @pytest.fixture(scope="module")

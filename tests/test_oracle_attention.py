@@ -182,3 +182,52 @@ def test_block_sparse_matches_brute_force(nq, nk, block, seed):
     fin = ~np.isneginf(lb)
     np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
     assert np.isneginf(lse[block:2 * block]).all() and (o[block:2 * block] == 0).all()
+
+
+def test_nan_reaches_exactly_the_rows_that_read_it():
+    """The NaN rule: a NaN in query row n, or in a K row that row n keeps, makes
+    all of O_n and LSE_n NaN (it enters every logit of that row, or one logit and
+    then the row's normaliser); a NaN in element c of a kept V row makes O_n[c]
+    NaN and leaves LSE_n alone; a row whose kept keys and query hold no NaN is
+    bitwise the clean result.  This is IEEE arithmetic applied to the masked
+    definition (Sparse VideoGen2 explainer, technical summary section 2.c:
+    only the selected blocks are read), checked here on the oracle."""
+    rng = np.random.default_rng(17)
+    nq, nk, block, d = 40, 36, 8, 6
+    q, k, v = (rng.standard_normal((n, d)) for n in (nq, nk, nk))
+    mask = rng.random((5, 5)) < 0.45
+    mask[np.arange(5), np.arange(5)] = True
+    mask[:, 0] = False                    # a key block that nobody keeps
+    mask[2] = False                       # a query block that keeps nothing
+    o0, l0 = oracle.block_sparse_attention(q, k, v, mask, block)
+    keeps = lambda j: np.repeat(mask[:, j // block], block)[:nq]   # noqa: E731
+    # NaN in one K row (of key block 3)
+    kn = k.copy()
+    kn[27, 4] = np.nan
+    o, lse = oracle.block_sparse_attention(q, kn, v, mask, block)
+    hit = keeps(27)
+    assert hit.any() and (~hit).any()
+    assert np.isnan(o[hit]).all() and np.isnan(lse[hit]).all()
+    assert np.array_equal(o[~hit], o0[~hit]) and np.array_equal(lse[~hit], l0[~hit])
+    # NaN in one V element (key block 1, column 2)
+    vn = v.copy()
+    vn[11, 2] = np.nan
+    o, lse = oracle.block_sparse_attention(q, k, vn, mask, block)
+    hit = keeps(11)
+    assert hit.any() and (~hit).any()
+    assert np.isnan(o[hit, 2]).all() and not np.isnan(np.delete(o, 2, axis=1)).any()
+    assert np.array_equal(o[~hit], o0[~hit]) and np.array_equal(lse, l0)
+    # NaN in one query row: that row only, even within its block
+    qn = q.copy()
+    qn[5, 0] = np.nan
+    o, lse = oracle.block_sparse_attention(qn, k, v, mask, block)
+    assert np.isnan(o[5]).all() and np.isnan(lse[5])
+    rest = np.arange(nq) != 5
+    assert np.array_equal(o[rest], o0[rest]) and np.array_equal(lse[rest], l0[rest])
+    # a NaN in a key block that no query block keeps changes nothing
+    kn = k.copy()
+    kn[0:8] = np.nan
+    vn = v.copy()
+    vn[0:8] = np.nan
+    o, lse = oracle.block_sparse_attention(q, kn, vn, mask, block)
+    assert np.array_equal(o, o0) and np.array_equal(lse, l0)
