@@ -1151,6 +1151,7 @@ __device__ int tile_union_ids(uint32_t m, int32_t *ids, int cap, int32_t *wsum) 
 // value being its virtual tile.  Queued and pair rows go to the workgroup's
 // region of tflags as in the main pass.
 constexpr int kUnionCap = 1024;                 // union ids held in LDS (more: every cluster)
+constexpr int kMaskTiles = 16;                  // union tiles whose candidate masks are kept
 template <int D>
 __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
     const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
@@ -1173,7 +1174,9 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
   __shared__ int32_t s_wsum[kCandWaves];
   __shared__ int32_t s_wq[kCandWaves], s_wp[kCandWaves];
   __shared__ int2 sRow[kCandTok];             // undecided rows: queued first, pairs last
-  __shared__ uint64_t sQid[kCandTok];         // listed candidate ids of queued rows
+  // per virtual tile (the first kMaskTiles) and token, each lane half's
+  // candidate slots: those whose value reached the half's running best - 2E
+  __shared__ uint16_t sCm[kMaskTiles][kCandTok][2];
   const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
   const int bh = xcd + 8 * (k8 / tph);
   const int tile = k8 % tph;
@@ -1271,12 +1274,11 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
                   0x1p-19f * (nx * cm + 0.5f * cm * cm);
   const float two_e = 2.f * 1.25f * e;
 
-  // candidates of the first two virtual tiles: slots whose value reaches this
-  // lane half's best so far minus 2E (a superset of those that reach the
-  // final best minus 2E, which hold the argmin)
+  // candidates: slots whose value reaches this lane half's best so far minus
+  // 2E (a superset of those that reach the final best minus 2E, which hold
+  // the argmin), kept in LDS for the first kMaskTiles virtual tiles
   float b1 = -INFINITY, b2 = -INFINITY, b3 = -INFINITY;
   int t1 = 0, t2 = 0;
-  uint32_t cmask[2] = {0u, 0u};
   auto compute = [&](auto bufc, int v) {
     constexpr int B = decltype(bufc)::value;
     f32x4 n4[4];
@@ -1307,12 +1309,12 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
     const bool new1 = b1 != p1;
     t2 = b2 == p2 ? t2 : ((new1 && b2 == p1) ? t1 : v);
     t1 = new1 ? v : t1;
-    if (v < 2) {
+    if (v < kMaskTiles) {   // uniform
       const float thr = b1 - two_e;
       uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m |= acc[i] >= thr ? (1u << acc_row(i, h)) : 0u;
-      cmask[v] = m;
+      for (int i = 0; i < 16; ++i) m |= acc[i] >= thr ? (1u << i) : 0u;
+      sCm[v][wave * 32 + col][h] = static_cast<uint16_t>(m);
     }
   };
 
@@ -1348,18 +1350,6 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
   if (h == 0 && tv && decided) as[tok] = ival;
   const bool queued = h == 0 && tv && !decided && !two;
   const bool paired = h == 0 && tv && two;
-  // a queued row with at most four candidates (both halves, at most two
-  // virtual tiles) lists their ids; otherwise the settle pass takes the union
-  const uint32_t m0 = cmask[0] | __shfl_xor(cmask[0], 32);
-  const uint32_t m1 = cmask[1] | __shfl_xor(cmask[1], 32);
-  const int ncand = nv <= 2 ? __popc(m0) + __popc(m1) : 99;
-  uint64_t listed = 0;
-  int nlisted = 0;
-  if (queued && ncand <= 4) {
-    for (int vv = 0; vv < 2; ++vv)
-      for (uint32_t m = vv ? m1 : m0; m; m &= m - 1, ++nlisted)
-        listed |= static_cast<uint64_t>(uid(vv * 32 + __builtin_ctz(m))) << (16 * nlisted);
-  }
   const uint64_t qm = __ballot(queued), pmk = __ballot(paired);
   if (lane == 0) {
     s_wq[wave] = __popcll(qm);
@@ -1375,20 +1365,16 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
     np += s_wp[w];
   }
   const uint64_t lt = (1ull << lane) - 1;
-  if (queued) {
-    const int at = q + __popcll(qm & lt);
-    sRow[at] = int2{tok, nlisted};
-    sQid[at] = listed;
-  }
+  if (queued) sRow[q + __popcll(qm & lt)] = int2{tok, wave * 32 + col};
   if (paired) sRow[kCandTok - 1 - (pp + __popcll(pmk & lt))] = int2{tok, (ival << 16) | ival2};
   __syncthreads();
 
   // Settle the undecided rows exactly, in fp64: a pair row compares its two
-  // clusters, a queued row the (up to four) clusters listed for it, or, when
-  // none were listed, every cluster of the union.  A group of 8 lanes per row
-  // (D/8 dimensions per lane, each lane's terms added in ascending order, the
-  // lanes in a fixed butterfly), four candidates loaded at a time; the
-  // smallest distance wins, ties to the lowest id.
+  // clusters, a queued row the slots its masks kept (unions of up to
+  // kMaskTiles tiles) or else every cluster of the union.  A group of 8 lanes
+  // per row (D/8 dimensions per lane, each lane's terms added in ascending
+  // order, the lanes in a fixed butterfly), four candidates loaded at a time;
+  // the smallest distance wins, ties to the lowest id.
   constexpr int LPR = 8;                     // lanes per row
   constexpr int DPL = D / LPR;               // dimensions per lane (8 or 16)
   constexpr int XQ = DPL / 8;                // 16-byte pieces of x per lane
@@ -1400,17 +1386,38 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
   for (int k = grp; k < nq + np; k += GPB) {   // uniform over the row's lanes
     const bool pair = k >= nq;
     const int2 e = pair ? sRow[kCandTok - 1 - (k - nq)] : sRow[k];
-    const uint64_t li = pair ? 0ull : sQid[k];
+    const bool masked = !pair && nv <= kMaskTiles;
+    // a queued row's full mask of tile t: the two halves' slots, slot i of
+    // half hh being row acc_row(i, hh) of the tile
+    auto tile_mask = [&](int t) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t mh = sCm[t][e.y][hh];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) m |= ((mh >> (4 * g)) & 15u) << (8 * g + 4 * hh);
+      }
+      return m;
+    };
+    int nmask = 0;
+    if (masked)
+      for (int t = 0; t < nv; ++t) nmask += __popc(tile_mask(t));
+    int cur_t = -1;
+    uint32_t cur_m = 0;
     u32x4 xv[XQ];
 #pragma unroll
     for (int i = 0; i < XQ; ++i)
       xv[i] = reinterpret_cast<const u32x4 *>(xb + static_cast<size_t>(e.x) * D)[sub * XQ + i];
-    const int cnt = pair ? 2 : (e.y > 0 ? e.y : nu);
+    const int cnt = pair ? 2 : (masked ? nmask : nu);
+    // called for j = 0, 1, 2, ... in order
     auto cand_id = [&](int j) {
       if (j >= cnt) return -1;
       if (pair) return j == 0 ? (e.y >> 16) & 0xffff : e.y & 0xffff;
-      if (e.y > 0) return static_cast<int>((li >> (16 * j)) & 0xffff);
-      return uid(j);
+      if (!masked) return uid(j);
+      while (cur_m == 0) cur_m = tile_mask(++cur_t);   // j < cnt: a set bit remains
+      const int b = __builtin_ctz(cur_m);
+      cur_m &= cur_m - 1;
+      return uid(cur_t * 32 + b);
     };
     double bd = INFINITY;
     int bi = 0x7fffffff;
