@@ -65,6 +65,20 @@ constexpr int kResTok = 64;                     // tokens per tile of the reside
 constexpr int kResWaves = 8;                    // waves per workgroup of the resident pass
 constexpr int kResTiles = 4;                    // centroid tiles (of 32) it holds per slice
 
+// p + the sum of squares of 8 bf16 values: each square is exact in fp32, each
+// addition rounds once (the values are widened by moving their bits, so the
+// arithmetic is explicit: plain fp32 multiply-adds)
+__device__ __forceinline__ float bf16x8_sumsq(bf16x8 v, float p) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = __uint_as_float(u[j] << 16), hi = __uint_as_float(u[j] & 0xffff0000u);
+    p = fmaf(lo, lo, p);
+    p = fmaf(hi, hi, p);
+  }
+  return p;
+}
+
 template <int D>
 __device__ __forceinline__ int cswz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
@@ -228,15 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void km_assign_main_kernel(
   for (int nt = 0; nt < NT; ++nt) {
     float p = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const u32x4 u = __builtin_bit_cast(u32x4, xf[nt][s2]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = u[j];
-        const bf16x2 v = __builtin_bit_cast(bf16x2, w);
-        p = __builtin_amdgcn_fdot2_f32_bf16(v, v, p, false);
-      }
-    }
+    for (int s2 = 0; s2 < NS; ++s2) p = bf16x8_sumsq(xf[nt][s2], p);
     p += __shfl_xor(p, 32);
     nx[nt] = sqrtf(p) * (1.f + 0x1p-10f) + 0x1p-60f;
   }
@@ -577,18 +583,11 @@ __global__ __launch_bounds__(64 * kResWaves, 1) void km_assign_res_kernel(
     for (int nt = 0; nt < 2; ++nt) {
       tok[nt] = base + nt * 32 + col;
       const bool tv = tok[nt] < n;
-      // ||x||^2 by bf16 pair dot products (exact products, fp32 sums); the
-      // 2^-60 covers products below the fp32 normal range if they are flushed
+      // ||x||^2 (exact products, fp32 sums); the 2^-60 covers products
+      // below the fp32 normal range if they are flushed
       float p = 0.f;
 #pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 u = __builtin_bit_cast(u32x4, xf[nt][s2]);
-          const uint32_t w = u[j];
-          const bf16x2 v = __builtin_bit_cast(bf16x2, w);
-          p = __builtin_amdgcn_fdot2_f32_bf16(v, v, p, false);
-        }
+      for (int s2 = 0; s2 < NS; ++s2) p = bf16x8_sumsq(xf[nt][s2], p);
       p += xor32(p);
       const float nx = sqrtf(p) * (1.f + 0x1p-10f) + 0x1p-60f;
       const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx * cm +
@@ -1259,14 +1258,7 @@ __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
   // the error bound of this token's values (x row norm, slice max ||c||)
   float px = 0.f;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const u32x4 u = __builtin_bit_cast(u32x4, xf[s]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x2 w2 = __builtin_bit_cast(bf16x2, u[j]);
-      px = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, px, false);
-    }
-  }
+  for (int s = 0; s < NS; ++s) px = bf16x8_sumsq(xf[s], px);
   px += __shfl_xor(px, 32);
   const float nx = sqrtf(px) * (1.f + 0x1p-10f) + 0x1p-60f;
   const float e = 0x1p-25f * cm * cm + 0x1p-18f * nx * cm +
