@@ -95,21 +95,49 @@ __global__ __launch_bounds__(kRadThreads) void radial_kernel(RadialParams p, int
   }
 }
 
-// One workgroup per (block, slice), one thread per column: the block's rows
-// summed in fp64 in row order, divided by the row count, stored as fp32.
-template <typename T>
-__global__ void block_means_kernel(const T *__restrict__ x, int n, int d, int block, int nb,
-                                   float *__restrict__ means, int32_t *__restrict__ sizes) {
-  const int b = blockIdx.x, s = blockIdx.y, col = threadIdx.x;
+// Block means: a thread owns one 16-byte piece of the row (8 bf16 or 4 fp32
+// columns) of one block and adds the block's rows into fp64 accumulators in
+// row order, eight rows' loads in flight; the sum divided by the row count is
+// stored as fp32.  A workgroup of kMeanThr threads covers kMeanThr / pieces
+// consecutive blocks of one slice.
+constexpr int kMeanThr = 256;
+template <typename T, int D>
+__global__ __launch_bounds__(kMeanThr) void block_means_kernel(
+    const T *__restrict__ x, int n, int block, int nb, float *__restrict__ means,
+    int32_t *__restrict__ sizes) {
+  constexpr int EPT = 16 / sizeof(T);          // columns per thread
+  constexpr int PPR = D / EPT;                 // threads per block (pieces per row)
+  constexpr int BPW = kMeanThr / PPR;          // blocks per workgroup
+  constexpr int U = 8;                         // rows in flight
+  const int s = blockIdx.y, tid = threadIdx.x;
+  const int b = blockIdx.x * BPW + tid / PPR, pc = tid % PPR;
+  if (b >= nb) return;
   const int r0 = b * block, r1 = min(n, r0 + block);
-  const T *base = x + (static_cast<size_t>(s) * n + r0) * d + col;
-  double acc = 0.0;
-  for (int r = r0; r < r1; ++r, base += d) {
-    if constexpr (sizeof(T) == 2) acc += static_cast<double>(bf16_bits_to_f32(*base));
-    else acc += static_cast<double>(*base);
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (static_cast<size_t>(s) * n + r0) * D) + pc;
+  double acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
+  for (int r = r0; r < r1; r += U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)   // (clamped: every load is in the block, all U in flight)
+      v[u] = src[static_cast<size_t>(min(r + u, r1 - 1) - r0) * PPR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = r + u < r1;   // rows past the block add +0 (no branch, so the loads stay ahead)
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        float f;
+        if constexpr (sizeof(T) == 2) f = bf16_bits_to_f32(static_cast<uint16_t>(v[u][e >> 1] >> (16 * (e & 1))));
+        else f = __uint_as_float(v[u][e]);
+        acc[e] += in ? static_cast<double>(f) : 0.0;
+      }
+    }
   }
-  means[(static_cast<size_t>(s) * nb + b) * d + col] = static_cast<float>(acc / (r1 - r0));
-  if (col == 0) sizes[static_cast<size_t>(s) * nb + b] = r1 - r0;
+  float *out = means + (static_cast<size_t>(s) * nb + b) * D + pc * EPT;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) out[e] = static_cast<float>(acc[e] / (r1 - r0));
+  if (pc == 0) sizes[static_cast<size_t>(s) * nb + b] = r1 - r0;
 }
 
 }  // namespace
@@ -124,13 +152,19 @@ hipError_t launch_radial_mask(const RadialParams &p, int32_t bh, uint8_t *mask,
 hipError_t launch_block_means(const void *x, int32_t dtype, int32_t bh, int32_t n, int32_t d,
                               int32_t block, float *means, int32_t *sizes, hipStream_t s) {
   const int nb = (n + block - 1) / block;
-  const dim3 grid(nb, bh);
-  if (dtype == SVA_BF16)
-    hipLaunchKernelGGL(block_means_kernel<uint16_t>, grid, dim3(d), 0, s,
-                       static_cast<const uint16_t *>(x), n, d, block, nb, means, sizes);
-  else
-    hipLaunchKernelGGL(block_means_kernel<float>, grid, dim3(d), 0, s,
-                       static_cast<const float *>(x), n, d, block, nb, means, sizes);
+  // blocks per workgroup: kMeanThr / (d / columns per thread)
+  auto grid = [&](int cols) { return dim3((nb + kMeanThr / (d / cols) - 1) / (kMeanThr / (d / cols)), bh); };
+#define SVA_MEANS(T, DD, COLS)                                                              \
+  hipLaunchKernelGGL((block_means_kernel<T, DD>), grid(COLS), dim3(kMeanThr), 0, s,          \
+                     static_cast<const T *>(x), n, block, nb, means, sizes)
+  if (dtype == SVA_BF16) {
+    if (d == 128) SVA_MEANS(uint16_t, 128, 8);
+    else SVA_MEANS(uint16_t, 64, 8);
+  } else {
+    if (d == 128) SVA_MEANS(float, 128, 4);
+    else SVA_MEANS(float, 64, 4);
+  }
+#undef SVA_MEANS
   return hipGetLastError();
 }
 
