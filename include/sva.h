@@ -32,6 +32,10 @@
  *   call only enqueues work on that stream and returns.
  * - dtype codes: SVA_F32 (IEEE fp32) or SVA_BF16 (bfloat16).  Supported head
  *   dims are 64 and 128.
+ * - Value arrays (Q, K, V, O, x, centroids and their permuted copies) are
+ *   read and written in 16-byte pieces and must be 16-byte aligned (any
+ *   allocation from hipMalloc or torch is); a misaligned one is refused with
+ *   SVA_EINVAL.  Index arrays and LSE need only their natural alignment.
  * - Errors: every argument is validated on the host before anything is
  *   launched.  A failed check returns SVA_EINVAL / SVA_EUNSUPPORTED /
  *   SVA_EWORKSPACE and launches nothing; a HIP launch failure returns

@@ -73,6 +73,25 @@ __device__ int block_reduce_imin(int v, int *red) {
   return r;
 }
 
+// sum over d of q[d] * k[d] in fp64, one fma per term in ascending d; the
+// fp32 row is read in 16-byte pieces, eight at a time
+template <int D>
+__device__ __forceinline__ double centroid_dot(const double *q, const float *k) {
+  const f32x4 *k4 = reinterpret_cast<const f32x4 *>(k);
+  double s = 0.0;
+#pragma unroll 1   // (unrolled, the compiler keeps all of q in registers across j)
+  for (int p0 = 0; p0 < D / 4; p0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = k4[p0 + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fma(q[4 * (p0 + u) + e], static_cast<double>(v[u][e]), s);
+  }
+  return s;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float *__restrict__ cent_q, const int32_t *__restrict__ size_q,
@@ -108,10 +127,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   double lmax = -INFINITY;
   int lvalid = 0;
   for (int j = tid; j < ck; j += kThreads) {
-    const float *kr = cent_k + (static_cast<size_t>(bh) * ck + j) * D;
-    double s = 0.0;
-    for (int d = 0; d < D; ++d) s = fma(sq[d], static_cast<double>(kr[d]), s);
-    s *= scale;
+    const double s = centroid_dot<D>(sq, cent_k + (static_cast<size_t>(bh) * ck + j) * D) * scale;
     key[j] = s;
     if (szk[j] > 0) {
       lmax = fmax(lmax, s);
@@ -250,10 +266,7 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(
   double best = -INFINITY;
   int best_j = 0x7fffffff;
   for (int j = tid; j < nk; j += kThreads) {
-    const float *kr = cent_k + (static_cast<size_t>(bh) * nk + j) * D;
-    double s = 0.0;
-    for (int d = 0; d < D; ++d) s = fma(sq[d], static_cast<double>(kr[d]), s);
-    s *= scale;
+    const double s = centroid_dot<D>(sq, cent_k + (static_cast<size_t>(bh) * nk + j) * D) * scale;
     const bool elig = szk[j] > 0 && (cand == nullptr || cand[static_cast<size_t>(i) * nk + j] != 0);
     const bool keep = elig && s >= theta;
     mk[j] = keep ? 1 : 0;

@@ -56,6 +56,13 @@ int32_t check_d(const char *fn, int32_t d) {
   return SVA_OK;
 }
 
+// value arrays (tensors, centroids) are read and written in 16-byte pieces
+int32_t check_a16(const char *fn, const char *what, const void *p) {
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(SVA_EINVAL, "%s: %s must be 16-byte aligned", fn, what);
+  return SVA_OK;
+}
+
 int32_t check_ws(const char *fn, size_t need, const void *ws, size_t ws_bytes) {
   if (ws_bytes < need)
     return fail(SVA_EWORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
@@ -89,6 +96,8 @@ int32_t sva_kmeans(const void *x, int32_t dtype, int32_t batch, int32_t heads, i
   const char *fn = "sva_kmeans";
   if (!x || !centroids || !assign || !sizes)
     return fail(SVA_EINVAL, "%s: x, centroids, assign and sizes must be non-NULL", fn);
+  SVA_TRY(check_a16(fn, "x", x));
+  SVA_TRY(check_a16(fn, "centroids", centroids));
   if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
   SVA_TRY(check_slices(fn, batch, heads, n));
   SVA_TRY(check_d(fn, d));
@@ -107,6 +116,8 @@ int32_t sva_cluster_spread(const void *x, int32_t dtype, int32_t batch, int32_t 
   const char *fn = "sva_cluster_spread";
   if (!x || !centroids || !assign || !spread)
     return fail(SVA_EINVAL, "%s: x, centroids, assign and spread must be non-NULL", fn);
+  SVA_TRY(check_a16(fn, "x", x));
+  SVA_TRY(check_a16(fn, "centroids", centroids));
   if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
   SVA_TRY(check_slices(fn, batch, heads, n));
   SVA_TRY(check_d(fn, d));
@@ -138,8 +149,11 @@ int32_t sva_permute(const int32_t *assign, int32_t c, int32_t batch, int32_t hea
     if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
     SVA_TRY(check_d(fn, d));
     if (!src || !dst) return fail(SVA_EINVAL, "%s: src and dst arrays must be non-NULL", fn);
-    for (int t = 0; t < n_tensors; ++t)
+    for (int t = 0; t < n_tensors; ++t) {
       if (!src[t] || !dst[t]) return fail(SVA_EINVAL, "%s: tensor pointer %d is NULL", fn, t);
+      SVA_TRY(check_a16(fn, "every tensor", src[t]));
+      SVA_TRY(check_a16(fn, "every tensor", dst[t]));
+    }
   }
   SVA_TRY(check_ws(fn, sva::sort_ws_bytes(batch * heads, n, c), ws, ws_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -179,6 +193,8 @@ int32_t sva_select_blocks(const float *cent_q, const int32_t *size_q, int32_t cq
   (void)ws_bytes;
   if (!cent_q || !size_q || !cent_k || !size_k || !mask || !kept_count || !kept_idx)
     return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_a16(fn, "cent_q", cent_q));
+  SVA_TRY(check_a16(fn, "cent_k", cent_k));
   SVA_TRY(check_slices(fn, batch, heads, 1));
   SVA_TRY(check_d(fn, d));
   if (cq < 1 || ck < 1) return fail(SVA_EINVAL, "%s: cq and ck must be >= 1", fn);
@@ -200,6 +216,8 @@ int32_t sva_select_threshold(const float *cent_q, const int32_t *size_q, int32_t
   const char *fn = "sva_select_threshold";
   if (!cent_q || !size_q || !cent_k || !size_k || !mask || !kept_count || !kept_idx)
     return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_a16(fn, "cent_q", cent_q));
+  SVA_TRY(check_a16(fn, "cent_k", cent_k));
   SVA_TRY(check_slices(fn, batch, heads, 1));
   SVA_TRY(check_d(fn, d));
   if (nq < 1 || nk < 1) return fail(SVA_EINVAL, "%s: nq and nk must be >= 1", fn);
@@ -250,6 +268,7 @@ int32_t sva_block_means(const void *x, int32_t dtype, int32_t batch, int32_t hea
                         int32_t d, int32_t block, float *means, int32_t *sizes, void *stream) {
   const char *fn = "sva_block_means";
   if (!x || !means || !sizes) return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_a16(fn, "x", x));
   if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
   SVA_TRY(check_slices(fn, batch, heads, n));
   SVA_TRY(check_d(fn, d));
@@ -263,6 +282,10 @@ static int32_t check_attn(const char *fn, const void *q, const void *k, const vo
                           int32_t dtype, int32_t batch, int32_t heads, int32_t n_q, int32_t n_k,
                           int32_t d, float scale, const void *o, int32_t o_dtype) {
   if (!q || !k || !v || !o) return fail(SVA_EINVAL, "%s: q, k, v and o must be non-NULL", fn);
+  SVA_TRY(check_a16(fn, "q", q));
+  SVA_TRY(check_a16(fn, "k", k));
+  SVA_TRY(check_a16(fn, "v", v));
+  SVA_TRY(check_a16(fn, "o", o));
   if (!dtype_ok(dtype) || !dtype_ok(o_dtype))
     return fail(SVA_EINVAL, "%s: bad dtype (%d) or o_dtype (%d)", fn, dtype, o_dtype);
   SVA_TRY(check_slices(fn, batch, heads, n_q));
@@ -403,6 +426,8 @@ int32_t sva_unpermute(const void *o_perm, const int32_t *perm, int32_t dtype, in
                       int32_t heads, int32_t n, int32_t d, void *o, void *stream) {
   const char *fn = "sva_unpermute";
   if (!o_perm || !perm || !o) return fail(SVA_EINVAL, "%s: NULL pointer argument", fn);
+  SVA_TRY(check_a16(fn, "o_perm", o_perm));
+  SVA_TRY(check_a16(fn, "o", o));
   if (!dtype_ok(dtype)) return fail(SVA_EINVAL, "%s: bad dtype %d", fn, dtype);
   SVA_TRY(check_slices(fn, batch, heads, n));
   SVA_TRY(check_d(fn, d));

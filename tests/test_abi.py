@@ -230,3 +230,24 @@ def test_debug_checks_switch(L):
             assert L.last_error().startswith("sva_block_sparse_attn")
     finally:
         assert lib.sva_set_debug_checks(0) == L.SVA_OK
+
+
+def test_value_arrays_must_be_16_byte_aligned(L):
+    """Value arrays are read in 16-byte pieces: a misaligned one is refused on
+    the host with SVA_EINVAL before anything is launched."""
+    lib = L.lib()
+    M = ctypes.c_void_p(264)   # 8 bytes past a 16-byte boundary
+    ws = lib.sva_attn_workspace_bytes(1, 2, 1000, 8)
+    ok = [P, P, P, 1, 1, 2, 1000, 1000, 128, P, 8, P, 8, P, P, 8, 0.1, P, 1, None, P, ws, None]
+    for i in (0, 1, 2, 17):               # q, k, v, o
+        args = list(ok)
+        args[i] = M
+        assert lib.sva_block_sparse_attn(*args) == L.SVA_EINVAL, i
+        assert "16-byte aligned" in L.last_error()
+    kws = lib.sva_kmeans_workspace_bytes(1, 2, 1000, 128, 10)
+    assert lib.sva_kmeans(M, 1, 1, 2, 1000, 128, 10, 3, P, P, P, None, P, kws, None) == L.SVA_EINVAL
+    assert lib.sva_kmeans(P, 1, 1, 2, 1000, 128, 10, 3, M, P, P, None, P, kws, None) == L.SVA_EINVAL
+    assert lib.sva_select_blocks(M, P, 4, P, P, 4, 1, 2, 128, 0.1, 0.9, P, P, P, None, 0,
+                                 None) == L.SVA_EINVAL
+    assert lib.sva_block_means(M, 1, 1, 2, 1000, 128, 128, P, P, None) == L.SVA_EINVAL
+    assert lib.sva_unpermute(M, P, 1, 1, 2, 10, 64, P, None) == L.SVA_EINVAL
