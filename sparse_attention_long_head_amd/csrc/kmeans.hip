@@ -1150,8 +1150,10 @@ __device__ int tile_union_ids(uint32_t m, int32_t *ids, int cap, int32_t *wsum) 
 // value being its virtual tile.  Queued and pair rows go to the workgroup's
 // region of tflags as in the main pass.
 constexpr int kUnionCap = 1024;                 // union ids held in LDS (more: every cluster)
-constexpr int kMaskTiles = 16;                  // union tiles whose candidate masks are kept
-template <int D>
+// union tiles whose candidate masks the candidate pass keeps: 16 (8 KB of LDS)
+// up to 16 tiles of clusters, 32 above (16 KB; two workgroups per CU)
+constexpr int kMaskTilesSmall = 16, kMaskTilesLarge = 32;
+template <int D, int kMaskTiles>
 __global__ __launch_bounds__(64 * kCandWaves) void km_assign_cand_kernel(
     const uint16_t *__restrict__ x, int n, int c, int cpad, const uint16_t *__restrict__ chi,
     const uint16_t *__restrict__ clo, const float *__restrict__ nh,
@@ -1747,9 +1749,13 @@ hipError_t run_kmeans(const KmeansArgs &a, hipStream_t s) {
       hipLaunchKernelGGL(km_tile_union_kernel, dim3(ctph, a.bh), dim3(64), 0, s, seg, nbr, a.n,
                          a.c, cpad, ctph, tun);
       SVA_CHECK(hipGetLastError());
-      hipLaunchKernelGGL((km_assign_cand_kernel<D>), cand_grid, dim3(64 * kCandWaves), 0, s,
-                         static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,
-                         a.centroids, perm, tun, a.assign, a.n_refined, a.bh, ctph);
+#define SVA_CAND(MT)                                                                         \
+  hipLaunchKernelGGL((km_assign_cand_kernel<D, MT>), cand_grid, dim3(64 * kCandWaves), 0, s,  \
+                     static_cast<const uint16_t *>(a.x), a.n, a.c, cpad, chi, clo, nh,        \
+                     a.centroids, perm, tun, a.assign, a.n_refined, a.bh, ctph)
+      if (cpad / 32 > kMaskTilesSmall) SVA_CAND(kMaskTilesLarge);
+      else SVA_CAND(kMaskTilesSmall);
+#undef SVA_CAND
       SVA_CHECK(hipGetLastError());
     } else if (bf16) {
       // the pair path (third best tracked) pays once the refine's re-scan is
