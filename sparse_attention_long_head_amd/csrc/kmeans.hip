@@ -1147,8 +1147,9 @@ __device__ int tile_union_ids(uint32_t m, int32_t *ids, int cap, int32_t *wsum) 
 // by direct global->LDS copies, the next tile's copies in flight while a tile
 // is computed.  Every value's tracking, error bound and decision (decided /
 // two candidates / queued) are those of km_assign_main_kernel, the tile of a
-// value being its virtual tile.  Queued and pair rows go to the workgroup's
-// region of tflags as in the main pass.
+// value being its virtual tile.  The pass then settles its own undecided rows
+// in fp64 (pair rows over their two clusters, queued rows over the slots
+// their per-tile candidate masks kept).
 constexpr int kUnionCap = 1024;                 // union ids held in LDS (more: every cluster)
 // union tiles whose candidate masks the candidate pass keeps: 16 (8 KB of LDS)
 // up to 16 tiles of clusters, 32 above (16 KB; two workgroups per CU)
