@@ -587,13 +587,20 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     // in two steps: wave 0 loads them into a register (a plain global load, a
     // step ahead), then stores the register into the stage.  sPerm is thus an
     // ordinary LDS array, and reading it needs no wait on the K/V copies in
-    // flight.  Past the end of the list the row of key 0 stands in.
+    // flight.  A key past the end of the list takes the original row of the
+    // chunk's first key (a kept row; row 0 of the slice when the whole chunk
+    // lies past the end), so every entry of a stage is the row its copy
+    // loads and the copy issue reads the stage alone, with no dependent read
+    // of the row map before it.
     int pnext = 0;
     auto perm_load = [&](int c) {
       if constexpr (PERM) {
         if (wave == 0) {
-          const int rr = c * kKT < L ? sWin[(c / kWin) & 1][(c % kWin) * kKT + lane] : -1;
-          pnext = pbase[rr < 0 ? 0 : rr];
+          const bool live = c * kKT < L;   // uniform
+          const int32_t *rows = sWin[(c / kWin) & 1] + (c % kWin) * kKT;
+          const int rr = live ? rows[lane] : -1;
+          const int r0 = live ? rows[0] : 0;
+          pnext = pbase[rr < 0 ? r0 : rr];
         }
       }
     };
@@ -603,9 +610,9 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       }
     };
     // the K/V source rows of this lane's copies of chunk cc (in stage st): the
-    // row map, then (PERM) the original rows.  Past the end of the list (the
-    // chunks after the last) whole stages are refilled from key 0's row, so
-    // every step issues the same number of copies.  Read a step before the
+    // row map, or (PERM) the stage's original rows.  Past the end of the list
+    // (the chunks after the last) whole stages are refilled from key 0's row,
+    // so every step issues the same number of copies.  Read a step before the
     // copies are issued, so the LDS latency hides behind that step's compute.
     struct ChunkRows {
       int phys[LPW];
@@ -615,13 +622,17 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       const bool live = cc * kKT < L;   // uniform
       const int32_t *rows = sWin[(cc / kWin) & 1] + (cc % kWin) * kKT;
       const int32_t *prow = sPerm[decltype(st)::value];
-      const int dummy = PERM ? prow[0] : (live ? max(rows[0], 0) : 0);
+      if constexpr (PERM) {
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int r = RPI * (wave * LPW + j) + ld_rsub;
-        int phys = live ? rows[r] : -1;
-        if constexpr (PERM) phys = phys < 0 ? -1 : prow[r];
-        cr.phys[j] = phys < 0 ? dummy : phys;
+        for (int j = 0; j < LPW; ++j) cr.phys[j] = prow[RPI * (wave * LPW + j) + ld_rsub];
+      } else {
+        const int dummy = live ? max(rows[0], 0) : 0;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+          const int r = RPI * (wave * LPW + j) + ld_rsub;
+          const int phys = live ? rows[r] : -1;
+          cr.phys[j] = phys < 0 ? dummy : phys;
+        }
       }
       return cr;
     };
