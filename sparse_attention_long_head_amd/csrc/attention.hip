@@ -30,8 +30,11 @@
 //   per-chunk sequence rotated by one phase -- PV(c-1), QK(c), softmax(c)
 //   against softmax(c-1), PV(c-1), QK(c) -- so one is in its MFMA phase while
 //   the other runs VALU work.
-// * Online softmax with a lazy rescale: the running max only moves (and O is
-//   only rescaled) when a row max exceeds it by more than 2^8, so P <= 256.
+// * Online softmax with a lazy rescale: the row max is taken on the first
+//   chunk of a kept-list segment; after that the exponentials are taken
+//   against the running max directly, and only when a lane's sum of P shows
+//   some P above 2^8 is the chunk's max taken, O rescaled and the chunk
+//   redone.  So P <= 32 * 2^8 and the max reduction leaves the common step.
 //   P is rounded to bf16 for the PV MFMA; max, sum and O accumulate in fp32.
 // * Sparse mode: one persistent workgroup per compute unit takes items from
 //   per-XCD queues (slices dealt to XCDs by total cost, each XCD working
@@ -405,6 +408,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
   constexpr int kWaveRows = kQTile / W;  // query rows per wave
   constexpr int NT = kWaveRows / 32;     // 32-query tiles per wave
   constexpr float kLazy = 8.f;           // rescale only when a row max grows by > 2^8
+  constexpr float kSumCap = 32.f * 256.f;  // a lane sum above this has some P > 2^kLazy
 
   constexpr int kStageBytes = kKT * D * 2;
   __shared__ __attribute__((aligned(16))) uint16_t sK[kStages][kKT * D];
@@ -699,7 +703,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       }
     };
     // online softmax of chunk cc: scores in sacc -> bf16 probabilities in pb,
-    // running max / sum updated, O rescaled when the max grows by > 2^kLazy
+    // running sum updated, max and O rescaled when the max grows by > 2^kLazy
     auto softmax = [&](int cc) {
       const int k0 = cc * kKT + mt_own * 32;   // key of m-tile 0, row 0
 #pragma unroll
@@ -715,50 +719,67 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
               if (k0 + mt * 32 + acc_row(i, h) >= L) sacc[nt][mt][i] = -INFINITY;
           }
         }
-        // (maximum, not maxnum: no NaN canonicalisation, so v_maximum3 does 2 per
-        // op); four independent chains keep the reduction short
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        // The row max is taken on the first chunk of a kept-list segment and
+        // otherwise only when a lane's probability sum exceeds 32 * 2^kLazy:
+        // then some p > 2^kLazy, so the max has grown by more than 2^kLazy
+        // and the chunk is redone after the rescale.  Between rescales every
+        // p stays <= 32 * 2^kLazy.
+        auto rescale = [&]() {
+          // (maximum, not maxnum: no NaN canonicalisation, so v_maximum3 does 2
+          // per op); four independent chains keep the reduction short
+          float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          if (mt == 1 && split) break;
+          for (int mt = 0; mt < 2; ++mt) {
+            if (mt == 1 && split) break;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            m4[i & 3] = __builtin_elementwise_maximum(m4[i & 3], sacc[nt][mt][i]);
-        }
-        float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]),
-                                                 __builtin_elementwise_maximum(m4[2], m4[3]));
-        {   // both lane halves hold the same query: exchange with permlane32_swap
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                           __float_as_uint(mx), false, false);
-          mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float mxs = mx * scale_log2;           // finite: the chunk has a key
-        if (__any(mxs > m_run[nt] + kLazy)) {
-          const float m_new = fmaxf(m_run[nt], mxs);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-          l_run[nt] *= alpha;
+            for (int i = 0; i < 16; ++i)
+              m4[i & 3] = __builtin_elementwise_maximum(m4[i & 3], sacc[nt][mt][i]);
+          }
+          float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]),
+                                                   __builtin_elementwise_maximum(m4[2], m4[3]));
+          {   // both lane halves hold the same query: exchange with permlane32_swap
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                             __float_as_uint(mx), false, false);
+            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          }
+          const float mxs = mx * scale_log2;
+          if (__any(mxs > m_run[nt] + kLazy)) {
+            const float m_new = fmaxf(m_run[nt], mxs);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+            l_run[nt] *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt)
+            for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
-          m_run[nt] = m_new;
-        }
+              for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+            m_run[nt] = m_new;
+          }
+        };
+        // p = 2^(s * scale_log2 - m) into pb; returns the lane's sum
         // (split: a key half may hold no key at all, the tail of the last
         // chunk; while the wave has seen no key its max stays -inf and the
         // exponent is taken against 0, giving p = 0)
-        const float m_sub = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
+        auto exps = [&]() {
+          const float m_sub = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+          float ps[4];   // four independent partial sums
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          if (mt == 1 && split) break;
+          for (int mt = 0; mt < 2; ++mt) {
+            if (mt == 1 && split) break;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_sub));
-            ps[i & 3] += p;
-            pb[nt][2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][i], scale_log2, -m_sub));
+              ps[i & 3] = (mt == 0 && i < 4) ? p : ps[i & 3] + p;
+              pb[nt][2 * mt + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+            }
           }
+          return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        };
+        if (cc == 0) rescale();
+        float tot = exps();
+        if (cc > 0 && __builtin_expect(__any(tot > kSumCap), 0)) {
+          rescale();
+          tot = exps();
         }
-        l_run[nt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        l_run[nt] += tot;
       }
     };
     // O^T += V^T P^T with the V rows in stage ST; the V operand (transposing

@@ -8,6 +8,8 @@ decision margin is below a stated tie threshold; such rows are counted.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -44,6 +46,9 @@ def rand_inputs(shape, seed, dtype="bf16", scale=1.0) -> np.ndarray:
 def check_attention(o: np.ndarray, ref: np.ndarray, bf16: bool, what: str = "") -> dict:
     err = np.abs(o.astype(np.float64) - ref)
     stats = dict(max=float(err.max()), mean=float(err.mean()))
+    if os.environ.get("SVA_PARITY_REPORT"):    # print the margins (run pytest with -s)
+        print(f"[parity] {what or 'attention'}: max-abs {stats['max']:.3g}, "
+              f"mean-abs {stats['mean']:.3g}")
     if bf16:
         assert stats["max"] <= BF16_MAX and stats["mean"] <= BF16_MEAN, (what, stats)
     else:
