@@ -566,25 +566,30 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     if (nch == 0) continue;   // uniform: L is shared
 
     // Row maps in windows of kWin chunks: the K row behind each virtual key
-    // of the window (-1 past the end).  All threads build a window at once, a
-    // branchless binary search over the range starts per key; windows w and
-    // w+1 are double-buffered, and window w+1 is built in the first step of
-    // window w.
+    // of the window (-1 past the end).  All threads build a window at once,
+    // each for two consecutive keys: a branchless binary search over the range
+    // starts (from the top bit of the range count) for the first, then at most
+    // one range forward for the second; windows w and w+1 are double-buffered,
+    // and window w+1 is built in the first step of window w.
     static_assert((kWin * kKT) % kThr == 0 && kLCap <= 1024, "window build geometry");
+    constexpr int KPT = kWin * kKT / kThr;   // consecutive window keys per thread
+    static_assert(KPT * kThr == kWin * kKT, "window keys split evenly over the threads");
+    const int bsearch0 = 1 << (31 - __clz(max(nseg, 1)));   // top bit of nseg (uniform)
     auto build_win = [&](int w) {
       int32_t *dst = sWin[w & 1];
+      const int v0 = w * (kWin * kKT) + KPT * tid;
+      int lo = 0;   // the last range starting at or before v0: largest j < nseg, sCum[j] <= v0
+      for (int b = bsearch0; b > 0; b >>= 1) {
+        const int j = lo + b;
+        const int cj = sCum[min(j, nseg)];
+        lo = (j < nseg && cj <= v0) ? j : lo;
+      }
 #pragma unroll
-      for (int u = 0; u < kWin * kKT / kThr; ++u) {
-        const int i = tid + u * kThr;
-        const int v = w * (kWin * kKT) + i;
-        int lo = 0;   // the last range starting at or before v: largest j < nseg, sCum[j] <= v
-#pragma unroll
-        for (int b = 512; b > 0; b >>= 1) {
-          const int j = lo + b;
-          const int cj = sCum[min(j, nseg)];
-          lo = (j < nseg && cj <= v) ? j : lo;
-        }
-        dst[i] = v < L ? sStart[lo] + (v - sCum[lo]) : -1;
+      for (int u = 0; u < KPT; ++u) {
+        const int v = v0 + u;
+        // ranges are non-empty: the next key is in the same range or the next one
+        if (u > 0 && lo + 1 < nseg && sCum[lo + 1] <= v) ++lo;
+        dst[KPT * tid + u] = v < L ? sStart[lo] + (v - sCum[lo]) : -1;
       }
     };
     // PERM: the original rows of a chunk's keys reach the chunk's sPerm stage
@@ -597,15 +602,16 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     // loads and the copy issue reads the stage alone, with no dependent read
     // of the row map before it.
     int pnext = 0;
+    auto perm_row = [&](int c) {   // (wave 0) the original row of the lane's key of chunk c
+      const bool live = c * kKT < L;   // uniform
+      const int32_t *rows = sWin[(c / kWin) & 1] + (c % kWin) * kKT;
+      const int rr = live ? rows[lane] : -1;
+      const int r0 = live ? rows[0] : 0;
+      return pbase[rr < 0 ? r0 : rr];
+    };
     auto perm_load = [&](int c) {
       if constexpr (PERM) {
-        if (wave == 0) {
-          const bool live = c * kKT < L;   // uniform
-          const int32_t *rows = sWin[(c / kWin) & 1] + (c % kWin) * kKT;
-          const int rr = live ? rows[lane] : -1;
-          const int r0 = live ? rows[0] : 0;
-          pnext = pbase[rr < 0 ? r0 : rr];
-        }
+        if (wave == 0) pnext = perm_row(c);
       }
     };
     auto perm_store = [&](auto st) {
@@ -668,15 +674,18 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     build_win(0);
     if (kWin < nch) build_win(1);
     __syncthreads();
-    perm_load(0);
-    perm_store(std::integral_constant<int, 0>{});
-    perm_load(1);
-    perm_store(std::integral_constant<int, 1>{});
-    perm_load(2);
-    perm_store(std::integral_constant<int, 2>{});
-    perm_load(3);
-    perm_store(std::integral_constant<int, 3>{});
-    perm_load(4);
+    if constexpr (PERM) {
+      if (wave == 0) {   // the five loads in flight together, then the four stores
+        int pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[j] = perm_row(j);
+        pnext = perm_row(4);
+        sPerm[0][lane] = pr[0];
+        sPerm[1][lane] = pr[1];
+        sPerm[2][lane] = pr[2];
+        sPerm[3][lane] = pr[3];
+      }
+    }
     lds_barrier();
     issue_loads(std::integral_constant<int, 0>{}, fetch_rows(std::integral_constant<int, 0>{}, 0));
     issue_loads(std::integral_constant<int, 1>{}, fetch_rows(std::integral_constant<int, 1>{}, 1));
