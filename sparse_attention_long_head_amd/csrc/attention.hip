@@ -657,12 +657,15 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
         const int phys = cr.phys[j];
         // (offsets stay in named variables: with an arithmetic expression in the
         // builtin's argument list, hipcc 7.2's host pass emits no launch stub)
-        const int koff = phys * D + ((ld_piece ^ kswz<D>(r)) << 3);
-        const int voff = phys * D + ((ld_piece ^ vswz<D>(r)) << 3);
-        __builtin_amdgcn_global_load_lds(kbase + koff,
+        // (unsigned 32-bit byte offsets from the slice base: scalar base + vector offset)
+        const uint32_t koff = static_cast<uint32_t>(phys) * (D * 2) + ((ld_piece ^ kswz<D>(r)) << 4);
+        const uint32_t voff = static_cast<uint32_t>(phys) * (D * 2) + ((ld_piece ^ vswz<D>(r)) << 4);
+        const char *ksrc = reinterpret_cast<const char *>(kbase) + koff;
+        const char *vsrc = reinterpret_cast<const char *>(vbase) + voff;
+        __builtin_amdgcn_global_load_lds(ksrc,
                                          (__attribute__((address_space(3))) void *)(dk + blk * 512),
                                          16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + voff,
+        __builtin_amdgcn_global_load_lds(vsrc,
                                          (__attribute__((address_space(3))) void *)(dv + blk * 512),
                                          16, 0, 0);
       }
@@ -961,7 +964,9 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     const int idx = sNext;
     if (idx < 0) break;                   // uniform: every thread read the same value
     const WorkItem it = lists[idx];
-    item(it.bh, it.qb, it.row0);
+    // (the item is the same for every lane: keep it, and the slice bases, scalar)
+    item(__builtin_amdgcn_readfirstlane(it.bh), __builtin_amdgcn_readfirstlane(it.qb),
+         __builtin_amdgcn_readfirstlane(it.row0));
     __syncthreads();                      // LDS and sNext are reused by the next item
   }
 }
