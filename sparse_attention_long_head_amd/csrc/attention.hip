@@ -421,7 +421,10 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
 
   __shared__ int32_t sNext;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform; made scalar for the fused-permutation kernels
+  // only (the other instantiations measured slower with it scalar)
+  const int wave = PERM ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int h = lane >> 5, col = lane & 31;
 
   // one work item: rows [row0, row0 + 256) of Q block qb of slice bh
