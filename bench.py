@@ -116,6 +116,9 @@ def main() -> int:
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-static", action="store_true",
+                    help="svg2 workload: skip the static-mask section (80%% and 85%% "
+                         "sparsity, dense on the same tensors)")
     ap.add_argument("--unfused", action="store_true",
                     help="materialise the permuted Q/K/V and unpermute O (instead of reading "
                          "and writing through the permutation inside attention)")
@@ -223,6 +226,7 @@ def main() -> int:
                  "speedup_whole_layer": dense_ms / ms_step}
 
     stage_roof = stage_rooflines(layer, t, iq, ik, cfg)
+    static = None if (args.no_static or args.config != "5s") else static_mask_summary(args)
 
     if args.copy_calibration:
         from sparse_attention_long_head_amd import sva_unpermute
@@ -272,9 +276,74 @@ def main() -> int:
                      "traffic": traffic},
         "cpu_baseline": cpu,
         "stage_rooflines": stage_roof,
+        "static_mask": static,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def static_mask_summary(args, sparsities=(0.8, 0.85), steps=5, warmup=2):
+    """The static-mask configuration timed inside the default run: i.i.d. N(0,1)
+    Q/K/V at the 5 s clip size, the radial candidate set padded with seeded
+    random tiles to exactly each sparsity (uniform 128-token blocks), block-sparse
+    attention alone, and dense attention on the same tensors for the speed-up."""
+    import torch
+
+    import synth
+    from sparse_attention_long_head_amd import lib, sva_block_sparse_attn, sva_full_attn
+
+    cfg = synth.CONFIGS["static"]
+    dev = torch.device("cuda:0")
+    log(f"[bench] static mask: {cfg.n} tokens x {cfg.heads} heads, sparsity {sparsities}")
+    x = synth.video_qkv(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in "qkv"}
+    del x
+    bh = cfg.batch * cfg.heads
+    scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
+    sizes = np.diff(synth.uniform_offsets(cfg.n, cfg.block)).astype(np.int64)
+    o = torch.empty_like(t["q"])
+    out = {"workload": f"static radial + random block mask, uniform {cfg.block}-token blocks, "
+                       "i.i.d. N(0,1) Q/K/V, block-sparse attention alone",
+           "tokens": cfg.n, "heads": cfg.heads, "head_dim": cfg.d}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    dense_ms = timed(lambda: sva_full_attn(t["q"], t["k"], t["v"], scale, o=o), args.dense_reps)
+    dflops = 4.0 * cfg.d * bh * cfg.n * cfg.n
+    out["dense"] = {"ms": round(dense_ms, 4),
+                    "frac_of_peak": round(dflops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    for sp in sparsities:
+        mask = synth.static_block_mask(cfg, sp)
+        count, idx = synth.mask_to_ell(mask)
+        nb = mask.shape[0]
+        off = torch.from_numpy(synth.uniform_offsets(cfg.n, cfg.block)).to(dev)
+        off = off.expand(cfg.batch, cfg.heads, nb + 1).contiguous()
+        kc = torch.from_numpy(count).to(dev).expand(cfg.batch, cfg.heads, nb).contiguous()
+        ki = torch.from_numpy(idx).to(dev).expand(cfg.batch, cfg.heads, nb, nb).contiguous()
+        ws = torch.empty(max(lib().sva_attn_workspace_bytes(cfg.batch, cfg.heads, cfg.n, nb), 1),
+                         dtype=torch.uint8, device=dev)
+        run = lambda: sva_block_sparse_attn(t["q"], t["k"], t["v"], off, off, kc, ki, scale,
+                                            o=o, ws=ws)
+        for _ in range(warmup):
+            run()
+        ms = timed(run, steps)
+        kept = int(sizes @ mask.astype(np.int64) @ sizes) * bh
+        tf = 4.0 * cfg.d * kept / (ms * 1e-3) / 1e12
+        out[f"sparsity_{sp:.2f}"] = {
+            "kept_tiles": int(mask.sum()), "tiles": int(nb * nb),
+            "density": round(kept / float(bh * cfg.n * cfg.n), 5), "ms": round(ms, 4),
+            "effective_tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "speedup_over_dense": round(dense_ms / ms, 3)}
+    return out
 
 
 def stage_rooflines(layer, t, iq, ik, cfg, reps=3):
