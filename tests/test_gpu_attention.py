@@ -238,6 +238,64 @@ def test_split_pairs_on_small_query_blocks(d):
     assert (o[0, 0, rows3] == 0).all() and np.isneginf(lse[0, 0, rows3]).all()
 
 
+def _growing_keys(k, jumps):
+    """Scale key rows so that the scores grow along the key sequence: every
+    64-key chunk c is multiplied by (1 + c), and the rows listed in ``jumps``
+    (row -> factor) further, rounded back to bf16."""
+    k = k.copy()
+    for c in range(-(-k.shape[-2] // 64)):
+        k[..., 64 * c:64 * (c + 1), :] *= 1.0 + c
+    for row, f in jumps.items():
+        k[..., row, :] *= f
+    return synth.round_bf16(k.astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", ["dense", "split", "perm"])
+def test_rescale_when_later_chunks_score_higher(mode):
+    # The running max is taken on a list's first chunk only, and again when a
+    # lane's sum of P shows some P above 2^8; then the chunk is redone.  Scores
+    # that grow chunk by chunk (and single keys 20x and 40x larger, whose P
+    # would be ~2^90 and overflow to inf against the stale max) force that
+    # path repeatedly, in the full, split (key halves) and permuted kernels.
+    d, heads = 128, 2
+    nq, nk = 256, 64 * 7 + 13
+    q = rand_inputs((1, heads, nq, d), 90, "bf16")
+    k = _growing_keys(rand_inputs((1, heads, nk, d), 91, "bf16"), {200: 20.0, 5 * 64 + 17: 40.0})
+    v = rand_inputs((1, heads, nk, d), 92, "bf16")
+    scale = 1 / math.sqrt(d)
+    T = torch.bfloat16
+    if mode == "dense":
+        o, lse = sva_full_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T), scale, want_lse=True)
+        refs = [oracle.full_attention(q[0, h], k[0, h], v[0, h], np.float32(scale))
+                for h in range(heads)]
+    else:
+        # two 128-row query blocks (split mode) or one 256-row block (perm),
+        # every key in one block that both keep
+        qs = [128, 128] if mode == "split" else [256]
+        qoff = np.tile(np.concatenate([[0], np.cumsum(qs)]).astype(np.int32), (1, heads, 1))
+        koff = np.tile(np.array([0, nk], np.int32), (1, heads, 1))
+        masks = np.ones((1, heads, len(qs), 1), bool)
+        cnt, idx = synth.mask_to_ell(masks)
+        args = (to_dev(qoff, torch.int32), to_dev(koff, torch.int32), to_dev(cnt, torch.int32),
+                to_dev(idx, torch.int32), scale)
+        if mode == "split":
+            o, lse = sva_block_sparse_attn(to_dev(q, T), to_dev(k, T), to_dev(v, T), *args,
+                                           want_lse=True)
+        else:
+            rng = np.random.default_rng(93)
+            pq = np.stack([rng.permutation(nq) for _ in range(heads)])[None].astype(np.int32)
+            pk = np.stack([rng.permutation(nk) for _ in range(heads)])[None].astype(np.int32)
+            o, lse = sva_block_sparse_attn_perm(to_dev(q, T), to_dev(k, T), to_dev(v, T),
+                                                to_dev(pq, torch.int32), to_dev(pk, torch.int32),
+                                                *args, want_lse=True)
+        refs = [oracle.full_attention(q[0, h], k[0, h], v[0, h], np.float32(scale))
+                for h in range(heads)]
+    o, lse = host(o), host(lse)
+    for h in range(heads):
+        check_attention(o[0, h], refs[h][0], True, f"{mode} head {h}")
+        check_lse(lse[0, h], refs[h][1], 1e-3 * max(1.0, float(np.abs(refs[h][1]).max()) / 100))
+
+
 def test_kept_list_longer_than_one_lds_segment():
     # 1300 two-key blocks, all kept: the kept list is walked in several segments
     rng = np.random.default_rng(5)
