@@ -287,6 +287,7 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
   __shared__ int32_t s_order[kMaxOrderHeads];        // slices by descending cost
   __shared__ int32_t s_hist[8][kOrderBuckets];       // counts, then write cursors
   __shared__ int32_t s_rank[kMaxOrderHeads];         // position among its XCD's slices
+  __shared__ int32_t s_cost[kMaxOrderHeads];         // cost of each slice, by rank
   __shared__ int32_t s_cnt[8], s_start[8];
   __shared__ int32_t s_group;                        // slices per sort group
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -303,18 +304,22 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
   };
   for (int i = t; i < 8 * kOrderBuckets; i += kOrderThreads) (&s_hist[0][0])[i] = 0;
   if (balance) {
-    // rank of each slice by (cost desc, index asc), then a greedy deal
+    // rank of each slice by (cost desc, index asc), then a greedy deal; the
+    // costs are staged in LDS first (s_x, rewritten by the deal)
+    for (int h = t; h < nbh; h += kOrderThreads) s_x[h] = hinfo[2 * h];
+    __syncthreads();
     for (int h = t; h < nbh; h += kOrderThreads) {
-      const int ch = hinfo[2 * h];
+      const int ch = s_x[h];
       int r = 0;
       for (int g = 0; g < nbh; ++g) {
-        const int cg = hinfo[2 * g];
+        const int cg = s_x[g];
         r += (cg > ch || (cg == ch && g < h)) ? 1 : 0;
       }
       s_order[r] = h;
+      s_cost[r] = ch;
     }
     __syncthreads();
-    if (t == 0) {
+    if (t == 0) {   // (serial, so it reads LDS only)
       long long load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       int dealt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int r = 0; r < nbh; ++r) {
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
         for (int x = 1; x < 8; ++x) best = load[x] < load[best] ? x : best;
         s_x[h] = best;
         s_rank[h] = dealt[best]++;
-        load[best] += hinfo[2 * h];
+        load[best] += s_cost[r];
       }
       int most = 1;
       for (int x = 0; x < 8; ++x) most = max(most, dealt[x]);
@@ -331,9 +336,20 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
     }
   }
   __syncthreads();
-  // histogram of the item keys per XCD
+  // histogram of the item keys per XCD; the first kHeld items of each thread
+  // stay in registers for the scatter below
   const size_t total = static_cast<size_t>(nbh) * work_cap;
-  for (size_t i = t; i < total; i += kOrderThreads) {
+  constexpr int kHeld = 16;
+  WorkItem held[kHeld];
+#pragma unroll
+  for (int u = 0; u < kHeld; ++u) {
+    const size_t i = t + static_cast<size_t>(u) * kOrderThreads;
+    held[u] = i < total ? work[i] : WorkItem{0, -1, -1, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kHeld; ++u)
+    if (held[u].qb >= 0) atomicAdd(&s_hist[xcd_of(held[u].bh)][key(held[u])], 1);
+  for (size_t i = t + static_cast<size_t>(kHeld) * kOrderThreads; i < total; i += kOrderThreads) {
     const WorkItem it = work[i];
     if (it.qb < 0) continue;
     atomicAdd(&s_hist[xcd_of(it.bh)][key(it)], 1);
@@ -371,12 +387,17 @@ __global__ __launch_bounds__(kOrderThreads) void attn_order_kernel(
     }
   }
   __syncthreads();
-  for (size_t i = t; i < total; i += kOrderThreads) {
-    const WorkItem it = work[i];
-    if (it.qb < 0) continue;
+  auto place = [&](const WorkItem &it) {
     const int x = xcd_of(it.bh);
     const int pos = atomicAdd(&s_hist[x][key(it)], 1);
     lists[s_start[x] + pos] = it;
+  };
+#pragma unroll
+  for (int u = 0; u < kHeld; ++u)
+    if (held[u].qb >= 0) place(held[u]);
+  for (size_t i = t + static_cast<size_t>(kHeld) * kOrderThreads; i < total; i += kOrderThreads) {
+    const WorkItem it = work[i];
+    if (it.qb >= 0) place(it);
   }
   if (t < 8) {
     ctl[t] = s_cnt[t];
