@@ -92,3 +92,52 @@ def test_output_sampled(long_layer, p):
                                                 host(layer.mask)[0, j].astype(bool),
                                                 np.float32(layer.scale), rows=rows)
         check_attention(host(layer.o)[0, j, rows], ro, True, f"{cfg.name} p={p} head {j}")
+
+
+@pytest.fixture(scope="module", params=[1.5, 2.0])
+def alpha_layer(request):
+    # the sweep's other centre scales (less / more separable content), one head
+    heads = (11,)
+    full = synth.CONFIGS["10s"]
+    cfg = full.with_(heads=len(heads), alpha=request.param)
+    x = synth.video_qkv(full, heads=heads, alpha=request.param)
+    iq = synth.gather_init(x["q"], synth.kmeans_init_indices(full, "q", cfg.cq, heads=heads))
+    ik = synth.gather_init(x["k"], synth.kmeans_init_indices(full, "k", cfg.ck, heads=heads))
+    t = {k: to_dev(v, torch.bfloat16) for k, v in x.items()}
+    layer = SparseVideoAttention(1, cfg.heads, cfg.n, cfg.d, cfg.cq, cfg.ck, cfg.iters, 0.9,
+                                 device=device())
+    layer(t["q"], t["k"], t["v"], to_dev(iq), to_dev(ik))
+    torch.cuda.synchronize()
+    return cfg, x, iq, ik, t, layer
+
+
+def test_alpha_points_lockstep_and_output(alpha_layer):
+    cfg, x, iq, ik, t, layer = alpha_layer
+    # last k-means iteration in lockstep with the oracle
+    ties = 0
+    for name, init, c, assign in (("q", iq, cfg.cq, layer.assign_q),
+                                  ("k", ik, cfg.ck, layer.assign_k)):
+        cent = to_dev(init)
+        sva_kmeans(t[name], c, cfg.iters - 1, cent)
+        before = host(cent).astype(np.float64)
+        _, a_last, _ = sva_kmeans(t[name], c, 1, cent)
+        assert torch.equal(a_last, assign)
+        ref, margin = oracle.assign_step(x[name][0, 0].astype(np.float64), before[0, 0])
+        ties += assign_parity(host(assign)[0, 0], ref, margin, f"alpha {cfg.alpha} {name}")
+    assert ties <= 5
+    # the selection in lockstep
+    _with_top_p(layer, t, 0.9)
+    r = oracle.top_p_select(oracle.centroid_scores(host(layer.cent_q)[0, 0],
+                                                   host(layer.cent_k)[0, 0], layer.scale),
+                            host(layer.sizes_q)[0, 0], host(layer.sizes_k)[0, 0], 0.9)
+    firm = r.cut_margin >= 1e-9
+    assert firm.mean() > 0.98
+    assert np.array_equal(host(layer.mask)[0, 0].astype(bool)[firm], r.mask[firm])
+    # sampled output rows under the GPU's clusters and mask
+    rows = np.unique(np.concatenate([[0, cfg.n - 1],
+                                     np.random.default_rng(5).integers(0, cfg.n, 40)]))
+    ro, _ = oracle.cluster_sparse_attention(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0],
+                                            host(layer.assign_q)[0, 0], host(layer.assign_k)[0, 0],
+                                            host(layer.mask)[0, 0].astype(bool),
+                                            np.float32(layer.scale), rows=rows)
+    check_attention(host(layer.o)[0, 0, rows], ro, True, f"alpha {cfg.alpha}")
