@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("n,c", [(1, 1), (100, 7), (2048, 2048), (5000, 300), (4097, 1),
-                                 (32760, 500), (32760, 100), (9000, 16384 // 4)])
+                                 (32760, 500), (32760, 100), (9000, 16384 // 4),
+                                 (20000, 8192), (20000, 10000)])
 def test_permutation_matches_oracle(n, c):
     heads = 3
     rng = np.random.default_rng(n + c)
