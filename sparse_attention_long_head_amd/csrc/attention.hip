@@ -422,8 +422,15 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
   constexpr int PPR = D / 8;             // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;          // rows per 1 KB direct-to-LDS wave load
   constexpr int kThr = 64 * W;
-  constexpr int LPW = PPR / W;           // such loads per wave per tensor per chunk
-  static_assert(LPW >= 1 && PPR % W == 0, "every wave copies whole 1 KB pieces");
+  // The K/V copies of a chunk are issued by waves CW .. W-1, LPC 1 KB loads per
+  // tensor each: with the fused permutation the late waves (which start each
+  // step with VALU work) issue them all, in the other instantiations every
+  // wave takes a share (measured: the late-wave split is 1% faster on the
+  // former and 7-8% slower on the others)
+  constexpr int CW = PERM ? W / 2 : 0;   // first copying wave
+  constexpr int LPC = PPR / (W - CW);    // loads per copying wave per tensor per chunk
+  static_assert(LPC >= 1 && PPR % (W - CW) == 0 && 2 * LPC < 16,
+                "copying waves take whole 1 KB pieces");
   constexpr int NS = D / 16;             // k-steps of the S MFMA
   constexpr int ND = D / 32;             // d tiles of the O accumulator
   constexpr int kWaveRows = kQTile / W;  // query rows per wave
@@ -617,16 +624,16 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       }
     };
     // PERM: the original rows of a chunk's keys reach the chunk's sPerm stage
-    // in two steps: wave 0 loads them into a register (a plain global load, a
-    // step ahead), then stores the register into the stage.  sPerm is thus an
-    // ordinary LDS array, and reading it needs no wait on the K/V copies in
-    // flight.  A key past the end of the list takes the original row of the
+    // in two steps: wave CW (the first copying wave) loads them into a
+    // register (a plain global load, a step ahead), then stores the register
+    // into the stage.  sPerm is thus an ordinary LDS array, and reading it
+    // needs no wait on the K/V copies in flight.  A key past the end of the list takes the original row of the
     // chunk's first key (a kept row; row 0 of the slice when the whole chunk
     // lies past the end), so every entry of a stage is the row its copy
     // loads and the copy issue reads the stage alone, with no dependent read
     // of the row map before it.
     int pnext = 0;
-    auto perm_row = [&](int c) {   // (wave 0) the original row of the lane's key of chunk c
+    auto perm_row = [&](int c) {   // (wave CW) the original row of the lane's key of chunk c
       const bool live = c * kKT < L;   // uniform
       const int32_t *rows = sWin[(c / kWin) & 1] + (c % kWin) * kKT;
       const int rr = live ? rows[lane] : -1;
@@ -635,12 +642,12 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     };
     auto perm_load = [&](int c) {
       if constexpr (PERM) {
-        if (wave == 0) pnext = perm_row(c);
+        if (wave == CW) pnext = perm_row(c);
       }
     };
     auto perm_store = [&](auto st) {
       if constexpr (PERM) {
-        if (wave == 0) sPerm[decltype(st)::value][lane] = pnext;
+        if (wave == CW) sPerm[decltype(st)::value][lane] = pnext;
       }
     };
     // the K/V source rows of this lane's copies of chunk cc (in stage st): the
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     // so every step issues the same number of copies.  Read a step before the
     // copies are issued, so the LDS latency hides behind that step's compute.
     struct ChunkRows {
-      int phys[LPW];
+      int phys[LPC];
     };
     auto fetch_rows = [&](auto st, int cc) {
       ChunkRows cr;
@@ -658,12 +665,12 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       const int32_t *prow = sPerm[decltype(st)::value];
       if constexpr (PERM) {
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) cr.phys[j] = prow[RPI * (wave * LPW + j) + ld_rsub];
+        for (int j = 0; j < LPC; ++j) cr.phys[j] = prow[RPI * ((wave - CW) * LPC + j) + ld_rsub];
       } else {
         const int dummy = live ? max(rows[0], 0) : 0;
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-          const int r = RPI * (wave * LPW + j) + ld_rsub;
+        for (int j = 0; j < LPC; ++j) {
+          const int r = RPI * ((wave - CW) * LPC + j) + ld_rsub;
           const int phys = live ? rows[r] : -1;
           cr.phys[j] = phys < 0 ? dummy : phys;
         }
@@ -675,8 +682,8 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       uint16_t *dk = sK[decltype(st)::value];
       uint16_t *dv = sV[decltype(st)::value];
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int blk = wave * LPW + j;
+      for (int j = 0; j < LPC; ++j) {
+        const int blk = (wave - CW) * LPC + j;
         const int r = RPI * blk + ld_rsub;
         const int phys = cr.phys[j];
         // (offsets stay in named variables: with an arithmetic expression in the
@@ -702,7 +709,7 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     if (kWin < nch) build_win(1);
     __syncthreads();
     if constexpr (PERM) {
-      if (wave == 0) {   // the five loads in flight together, then the four stores
+      if (wave == CW) {   // the five loads in flight together, then the four stores
         int pr[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) pr[j] = perm_row(j);
@@ -714,9 +721,12 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
       }
     }
     lds_barrier();
-    issue_loads(std::integral_constant<int, 0>{}, fetch_rows(std::integral_constant<int, 0>{}, 0));
-    issue_loads(std::integral_constant<int, 1>{}, fetch_rows(std::integral_constant<int, 1>{}, 1));
-    ChunkRows nxt = fetch_rows(std::integral_constant<int, 2>{}, 2);
+    ChunkRows nxt{};
+    if (wave >= CW) {
+      issue_loads(std::integral_constant<int, 0>{}, fetch_rows(std::integral_constant<int, 0>{}, 0));
+      issue_loads(std::integral_constant<int, 1>{}, fetch_rows(std::integral_constant<int, 1>{}, 1));
+      nxt = fetch_rows(std::integral_constant<int, 2>{}, 2);
+    }
 
     // S^T = K Q^T for the 64 keys of the chunk in stage ST (two 32-key m-tiles)
     // x the wave's query tiles; each K fragment serves every query tile
@@ -870,18 +880,21 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
     auto step = [&](auto st, int c) {
       constexpr int S = decltype(st)::value;
       constexpr int SP = (S + kStages - 1) % kStages;   // stage of chunk c-1
-      // chunk c has landed once only chunk c+1's copies are outstanding; after
-      // the barrier every wave's copies of chunk c are in LDS and every wave is
+      // chunk c has landed once only chunk c+1's copies are outstanding (a
+      // wave that copies nothing waits for nothing); after the barrier every
+      // copying wave's part of chunk c is in LDS and every wave is
       // done with chunk c-2, whose stage chunk c+2 then refills
-      // (PERM: wave 0's load of chunk c+4's original rows is older than chunk
+      // (PERM: wave CW's load of chunk c+4's original rows is older than chunk
       // c+1's K/V copies, so it has landed too)
-      wait_vmcnt<2 * LPW>();
+      wait_vmcnt<2 * LPC>();
       lds_barrier();
       if (c % kWin == 0 && (c / kWin + 1) * kWin < nch) build_win(c / kWin + 1);
       perm_store(st);                 // chunk c+4 (its stage is chunk c's)
       perm_load(c + 5);
-      issue_loads(std::integral_constant<int, (S + 2) % kStages>{}, nxt);
-      nxt = fetch_rows(std::integral_constant<int, (S + 3) % kStages>{}, c + 3);
+      if (wave >= CW) {
+        issue_loads(std::integral_constant<int, (S + 2) % kStages>{}, nxt);
+        nxt = fetch_rows(std::integral_constant<int, (S + 3) % kStages>{}, c + 3);
+      }
 
       if (wave_active) {
         if (late && c > 0) softmax(c - 1);
