@@ -69,7 +69,7 @@ constexpr int attn_waves() { return 8; }
 constexpr int kKT = 64;           // keys per chunk
 constexpr int kStages = 4;        // K/V chunk buffers in LDS (two in flight, two in use)
 constexpr int kLCap = 1024;       // kept-list entries staged in LDS at a time
-constexpr int kWin = 16;          // chunks per row-map window
+constexpr int kWin = 32;          // chunks per row-map window
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -598,10 +598,10 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(
 
     // Row maps in windows of kWin chunks: the K row behind each virtual key
     // of the window (-1 past the end).  All threads build a window at once,
-    // each for two consecutive keys: a branchless binary search over the range
+    // each for KPT consecutive keys: a branchless binary search over the range
     // starts (from the top bit of the range count) for the first, then at most
-    // one range forward for the second; windows w and w+1 are double-buffered,
-    // and window w+1 is built in the first step of window w.
+    // one range forward per further key; windows w and w+1 are
+    // double-buffered, and window w+1 is built in the first step of window w.
     static_assert((kWin * kKT) % kThr == 0 && kLCap <= 1024, "window build geometry");
     constexpr int KPT = kWin * kKT / kThr;   // consecutive window keys per thread
     static_assert(KPT * kThr == kWin * kKT, "window keys split evenly over the threads");
